@@ -1,0 +1,199 @@
+/*
+ * gemm_mi355x.h - C ABI of the MI355X (gfx950) batched GEMM with fused epilogue.
+ *
+ *   D       = alpha * A x B + beta * C          (the pre-activation output)
+ *   PostAct = act(alpha * A x B + beta * C)
+ *
+ * The operation is the one defined by the quack-kernels pages (0.1.10 -> 0.2.0 diff):
+ *   - page 5, quack/dense_gemm_sm90.py: the gemm_sm90 wrapper takes A (l, m, k), B (l, n, k),
+ *     D and C (l, m, n); GemmSm90.epi_visit_acc_subtile scales the fp32 accumulator by alpha
+ *     and adds beta * C (beta absent means +C);
+ *   - page 6, quack/gemm_act_sm90.py: GemmActSm90.epi_visit_acc_subtile applies the
+ *     activation to that same fp32 value and writes it as PostAct next to D; act_fn_map lists
+ *     relu, relu_sq and gelu_tanh_approx;
+ *   - page 5, GemmSm90.__call__ and kernel: the varlen-M (grouped) mode, where cu_seqlens_m
+ *     splits the rows of A / C / D into groups and group g multiplies by its own B[g];
+ *   - page 5, GemmSm90.is_valid_dtypes: fp16 / bf16 / e4m3 / e5m2 inputs, fp32 accumulation,
+ *     fp8 operands K-major only.
+ * SiLU is an addition of this library (x * sigmoid(x)).
+ *
+ * Conventions used by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or retains them. gemm_run writes only D, PostAct and (debug) the
+ *     tile log; it reads A, B, C, alpha/beta pointers and cu_seqlens_m.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Launches are
+ *     asynchronous; no entry point synchronises a stream or the device.
+ *   - Errors are returned as gemm_status, never thrown; gemm_last_error() gives a
+ *     thread-local message describing the last failure on the calling thread.
+ *   - A gemm_plan holds host memory only. gemm_create makes no HIP call. A plan may be used
+ *     from several threads and streams at once (gemm_run does not modify it).
+ */
+#ifndef GEMM_MI355X_H
+#define GEMM_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, inconsistent strides  */
+  GEMM_ERR_UNSUPPORTED = 2, /* valid request this library does not implement          */
+  GEMM_ERR_ALIGNMENT = 3,   /* contiguous dimension / pointer not 16-byte aligned     */
+  GEMM_ERR_HIP = 4,         /* a HIP runtime call failed (message in gemm_last_error) */
+  GEMM_ERR_NO_MEMORY = 5    /* host allocation of the plan failed                    */
+} gemm_status;
+
+typedef enum {
+  GEMM_DT_NONE = 0, /* operand absent (C, D or PostAct only)          */
+  GEMM_DT_F16 = 1,  /* IEEE binary16                                  */
+  GEMM_DT_BF16 = 2, /* bfloat16                                       */
+  GEMM_DT_F32 = 3,  /* IEEE binary32 (C, D, PostAct only)             */
+  GEMM_DT_E4M3 = 4, /* OCP fp8 E4M3 ("fn": no inf, max 448)           */
+  GEMM_DT_E5M2 = 5  /* OCP fp8 E5M2 (IEEE-like inf/NaN, max 57344)    */
+} gemm_dtype;
+
+/* Which logical dimension is contiguous in memory (page 5, gemm_sm90: majors from strides).
+ *   A (l, m, k):  GEMM_ROW = K contiguous ("K-major"):  A[l*sa + m*lda + k]
+ *                 GEMM_COL = M contiguous ("M-major"):  A[l*sa + k*lda + m]
+ *   B (l, n, k):  GEMM_ROW = K contiguous:              B[l*sb + n*ldb + k]
+ *                 GEMM_COL = N contiguous:              B[l*sb + k*ldb + n]
+ *   C, D, PostAct (l, m, n):
+ *                 GEMM_ROW = N contiguous:              X[l*sx + m*ldx + n]
+ *                 GEMM_COL = M contiguous:              X[l*sx + n*ldx + m]            */
+typedef enum { GEMM_ROW = 0, GEMM_COL = 1 } gemm_major;
+
+/* Activation applied to the fp32 pre-activation value to form PostAct
+ * (page 6, gemm_act_sm90.py, act_fn_map; SiLU added by this library). */
+typedef enum {
+  GEMM_ACT_NONE = 0,      /* PostAct = pre                                            */
+  GEMM_ACT_RELU = 1,      /* max(pre, 0)                                              */
+  GEMM_ACT_RELU_SQ = 2,   /* max(pre, 0)^2                                            */
+  GEMM_ACT_GELU_TANH = 3, /* pre/2 * (1 + tanh(sqrt(2/pi) * (pre + 0.044715 pre^3)))  */
+  GEMM_ACT_SILU = 4       /* pre / (1 + exp(-pre))                                    */
+} gemm_act;
+
+/* Problem description. Sizes and strides are in ELEMENTS.
+ *
+ * Dense batched mode (varlen_m == 0): A is (L, M, K), B is (L, N, K), C/D/PostAct are
+ * (L, M, N); sa/sb/sc/sd/sp are the batch strides (ignored when L == 1).
+ *
+ * Varlen-M mode (varlen_m == 1, page 5, GemmSm90 with VarlenMTileScheduler): L is the
+ * number of groups G and M the total number of rows. A is (M, K), C/D/PostAct are (M, N),
+ * B is (G, N, K) with batch stride sb; cu_seqlens_m (passed to gemm_run, device int32[G+1])
+ * gives the row range [cu[g], cu[g+1]) of group g. sa/sc/sd/sp are ignored.
+ *
+ * Types: a, b in {F16, BF16, E4M3, E5M2}. 16-bit inputs need a == b; 8-bit inputs may mix
+ * E4M3 and E5M2 and must both be GEMM_ROW (K-major) (page 5, is_valid_dtypes).
+ * c, d, post in {NONE, F16, BF16, F32}; at least one of d, post is not NONE.
+ * The C term is present iff c != NONE; beta multiplies it (beta = 1 gives +C; beta = 0
+ * still reads C, so NaN/inf in C propagate).
+ * C, D and PostAct that are present must share one major mode.
+ * Varlen mode supports only GEMM_ROW outputs.
+ *
+ * Alignment (page 5, constraints of the dense GEMM docstring): the contiguous dimension
+ * of every operand must hold a whole number of 16-byte chunks (a multiple of 8 elements
+ * for 16-bit types, 16 for fp8, 4 for f32), and every leading-dimension and batch stride
+ * must be a multiple of 16 bytes. Pointers must be 16-byte aligned (checked by gemm_run).
+ *
+ * Tuning fields (0 = library default):
+ *   tile_m, tile_n  output tile per workgroup; supported pairs: 256x256, 128x128.
+ *   group_m         raster group size G of the tile map, power of two in [1, 16], default 8.
+ *   max_ctas        cap on the persistent grid size.
+ *   xcd_remap       -1: off, 0: default (on), 1: on. See gemm_plan_grid.                 */
+typedef struct {
+  int32_t M, N, K, L;
+  int32_t a, b, c, d, post;                              /* gemm_dtype */
+  int32_t a_major, b_major, c_major, d_major, post_major; /* gemm_major */
+  int64_t lda, ldb, ldc, ldd, ldp;
+  int64_t sa, sb, sc, sd, sp;
+  float alpha, beta;
+  int32_t act;      /* gemm_act */
+  int32_t varlen_m; /* 0 or 1 */
+  int32_t tile_m, tile_n;
+  int32_t group_m;
+  int32_t max_ctas;
+  int32_t xcd_remap;
+} gemm_desc;
+
+typedef struct gemm_plan gemm_plan;
+
+/* Validate `desc` and build a plan (host memory only, no HIP call). On success *out owns a
+ * new plan to release with gemm_destroy; on failure *out is set to NULL and the status
+ * says why: INVALID_ARG (NULL desc/out, M/N/L <= 0, K < 0, strides smaller than the
+ * extents they skip, unknown enum value), UNSUPPORTED (dtype or major combination the
+ * pages exclude or this library does not build, tile pair not offered, tile count >= 2^31,
+ * a tile's operand byte offsets >= 2^31), ALIGNMENT (contiguous extent or stride not a
+ * multiple of 16 bytes), NO_MEMORY. K == 0 is valid: the product is then zero
+ * (page 5, GemmSm90.mma sets the accumulator to zero when there is no k-tile). */
+gemm_status gemm_create(const gemm_desc* desc, gemm_plan** out);
+
+/* Enqueue the GEMM on `stream`. A, B, D / PostAct (those the plan declares present) must
+ * be non-NULL device pointers; C must be non-NULL iff the plan has a C type.
+ * alpha_dev / beta_dev: optional device pointers to one fp32 each; when non-NULL they
+ * replace desc.alpha / desc.beta and are read by the kernel at run time (page 5,
+ * gemm_sm90 passes a tensor alpha/beta to the kernel as a pointer).
+ * cu_seqlens_m: device int32[L+1], required iff varlen_m; precondition (not checked):
+ * cu[0] == 0, non-decreasing, cu[L] == M. Returns INVALID_ARG for a missing pointer,
+ * ALIGNMENT for a pointer that is not 16-byte aligned, HIP if the launch fails. */
+gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
+                     void* PostAct, const float* alpha_dev, const float* beta_dev,
+                     const int32_t* cu_seqlens_m, void* stream);
+
+/* As gemm_run, and additionally record the persistent schedule: for workgroup b and its
+ * i-th tile (i < max_iters) the kernel writes int32 {m_blk, n_blk, l, t} at
+ * tile_log[(b * max_iters + i) * 4]; entries it does not reach are left untouched
+ * (callers pre-fill them). For varlen plans l is the group and m_blk the block inside it.
+ * tile_log is a device buffer of at least P * max_iters * 4 int32 (P from gemm_plan_grid
+ * with the device's CU count). Used to check the tile map bit for bit. */
+gemm_status gemm_run_logged(const gemm_plan* plan, const void* A, const void* B, const void* C,
+                            void* D, void* PostAct, const float* alpha_dev, const float* beta_dev,
+                            const int32_t* cu_seqlens_m, int32_t* tile_log, int32_t max_iters,
+                            void* stream);
+
+/* Release a plan (NULL is accepted). */
+gemm_status gemm_destroy(gemm_plan* plan);
+
+/* The schedule a plan uses on a device with `num_cus` compute units:
+ *   tile_m, tile_n: the output tile; group_m: raster group G; xcd_remap: 0/1;
+ *   tiles: T = ceil(M/tile_m) * ceil(N/tile_n) * L for dense plans, -1 for varlen plans
+ *          (their T depends on cu_seqlens_m, known only on the device);
+ *   grid:  P = min(T, num_cus * workgroups_per_cu) (varlen: num_cus * workgroups_per_cu).
+ * Workgroup b handles linear tiles t = b' + i * P while t < T, where b' = b, or with the
+ * XCD remap and P % 8 == 0, b' = (b % 8) * (P / 8) + b / 8. Tile t maps to (m_blk, n_blk,
+ * l) by the grouped raster of page 5 (the removed 0.1.10 "CTA swizzle" in GemmSm90.kernel):
+ * l = t / (tm * tn); inside a batch, groups of G M-blocks with M fastest, then N, then the
+ * next group; the tm % G leftover M-blocks form a last group of that width. Varlen plans
+ * concatenate the groups' tiles in group order (ceil(M_g / tile_m) * tn tiles each) and use
+ * the same raster inside a group. All device divisions use FastDivmod (page 6,
+ * quack/fast_math.py). Any output pointer may be NULL. */
+gemm_status gemm_plan_grid(const gemm_plan* plan, int32_t num_cus, int32_t* tile_m,
+                           int32_t* tile_n, int32_t* group_m, int32_t* xcd_remap,
+                           int64_t* tiles, int32_t* grid);
+
+/* FastDivmod constants the library computes for divisor d (1 <= d < 2^31), as page 6,
+ * quack/fast_math.py, FastDivmod.create: p = 31 + ceil(log2 d),
+ * multiplier = ceil(2^p / d) (as uint32), shift = p - 32. */
+gemm_status gemm_fastdivmod_params(uint32_t d, uint32_t* multiplier, uint32_t* shift);
+
+/* Device self-check of the library's FastDivmod: for every d in [d_lo, d_hi] and
+ * n in [0, n_count) the kernel compares the library's quotient/remainder with the device's
+ * integer '/' and '%', and atomically adds the number of mismatching pairs to *bad_dev
+ * (device uint64, not cleared by the call). Requires 1 <= d_lo <= d_hi < 2^31 and
+ * n_count <= 2^31. */
+gemm_status gemm_fastdivmod_check(uint32_t d_lo, uint32_t d_hi, uint32_t n_count,
+                                  unsigned long long* bad_dev, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* gemm_status_string(gemm_status status);
+
+/* Message about the last failure on the calling thread ("" if none). */
+const char* gemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_MI355X_H */

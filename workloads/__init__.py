@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs for the GEMM workloads (shared by the tests, the smoke check and
+the benchmark; holds no GEMM arithmetic).
+
+Values are drawn in float64 with numpy's PCG64 and stored in the operand type with torch's
+CPU casts. Seeds follow the pages' example harness (page 5, quack/dense_gemm_sm90.py, the
+removed 0.1.10 run(): torch.manual_seed(1111)): seed = 1111 + 10 * workload_index + slot,
+slot A = 0, B = 1, C = 2, group sizes = 3.
+
+Every generator returns an `Inputs` with CPU tensors:
+  store_*   the contiguous storage tensor in the operand type;
+  A, B, C   logical views: A (L, M, K), B (L, N, K), C (L, M, N) (varlen: A (M, K),
+            B (G, N, K), C (M, N)); an M-major A is a permuted view of a [L][K][M] store.
+plus the scalars of the problem (alpha, beta, activation, cu_seqlens_m, output types).
+"""
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32,
+            "e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+CODE_DT = {"f16": torch.int16, "bf16": torch.int16, "f32": torch.int32,
+           "e4m3": torch.uint8, "e5m2": torch.uint8}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+@dataclass
+class Inputs:
+    name: str
+    M: int
+    N: int
+    K: int
+    L: int
+    a_dt: str
+    b_dt: str
+    A: torch.Tensor
+    B: torch.Tensor
+    C: Optional[torch.Tensor] = None
+    c_dt: str = "none"
+    d_dt: str = "none"
+    post_dt: str = "none"
+    alpha: float = 1.0
+    beta: float = 1.0
+    act: str = "none"
+    cu_seqlens: Optional[np.ndarray] = None
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def varlen(self) -> bool:
+        return self.cu_seqlens is not None
+
+    def flops(self) -> float:
+        if self.varlen:
+            return 2.0 * self.M * self.N * self.K
+        return 2.0 * self.M * self.N * self.K * self.L
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def to_dtype(x: np.ndarray, dt: str) -> torch.Tensor:
+    """Store float64 values in operand type `dt` (torch CPU cast)."""
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dt in ("e4m3", "e5m2"):
+        t = t.clamp(-FP8_MAX[dt], FP8_MAX[dt]).to(torch.float32)
+    return t.to(TORCH_DT[dt])
+
+
+def uniform(seed, shape, dt):
+    return to_dtype(rng(seed).uniform(-1.0, 1.0, size=shape), dt)
+
+
+def normal(seed, shape, dt, std=1.0):
+    return to_dtype(rng(seed).standard_normal(size=shape) * std, dt)
+
+
+def quantize_fp8(seed, shape, dt):
+    """Per-tensor scaled fp8: s = amax|X| / fmax, codes = X / s stored in fp8 (saturating).
+    Returns (codes tensor, scale s as a Python float)."""
+    x = rng(seed).standard_normal(size=shape)
+    s = float(np.max(np.abs(x))) / FP8_MAX[dt]
+    return to_dtype(x / s, dt), s
+
+
+def codes_of(t: torch.Tensor) -> np.ndarray:
+    """Raw stored codes of a tensor (its whole storage from its storage offset, flat)."""
+    base = t
+    while base._base is not None:
+        base = base._base
+    flat = base.reshape(-1)
+    return flat.view(CODE_DT[_dt_name(flat.dtype)]).numpy().view(_np_code(flat.dtype))
+
+
+def _dt_name(tdt):
+    for k, v in TORCH_DT.items():
+        if v == tdt:
+            return k
+    raise KeyError(tdt)
+
+
+def _np_code(tdt):
+    return {torch.float16: np.uint16, torch.bfloat16: np.uint16, torch.float32: np.uint32,
+            torch.float8_e4m3fn: np.uint8, torch.float8_e5m2: np.uint8}[tdt]
+
+
+# ---------------------------------------------------------------------------------------
+# helpers to build operands in a given major mode
+# ---------------------------------------------------------------------------------------
+
+def make_a(gen, L, M, K, m_major, seed, dt, **kw):
+    """Logical A (L, M, K); storage [L][M][K] (K-major) or [L][K][M] (M-major)."""
+    if m_major:
+        store = gen(seed, (L, K, M), dt, **kw)
+        return store.permute(0, 2, 1)
+    return gen(seed, (L, M, K), dt, **kw)
+
+
+def make_b(gen, L, N, K, n_major, seed, dt, **kw):
+    if n_major:
+        store = gen(seed, (L, K, N), dt, **kw)
+        return store.permute(0, 2, 1)
+    return gen(seed, (L, N, K), dt, **kw)
+
+
+# ---------------------------------------------------------------------------------------
+# the five workloads (sizes as in the project's workload list)
+# ---------------------------------------------------------------------------------------
+
+def plain_256():
+    """Plain GEMM 256^3, fp16 in, fp16 D, U[-1, 1), alpha = 1, no C, no activation."""
+    s = 1111 + 10 * 0
+    M = N = K = 256
+    A = uniform(s + 0, (1, M, K), "f16")
+    B = uniform(s + 1, (1, N, K), "f16")
+    return Inputs("plain_256_f16", M, N, K, 1, "f16", "f16", A, B, d_dt="f16")
+
+
+def act_4096(beta=0.5, act="gelu_tanh", c=True, gemm_scale=None):
+    """4096^3 bf16, A/B ~ N(0,1)/sqrt(K), C ~ N(0,1), beta = 0.5, GELU-tanh, D and PostAct."""
+    s = 1111 + 10 * 1
+    M = N = K = 4096
+    std = 1.0 / np.sqrt(K) if gemm_scale is None else gemm_scale
+    A = normal(s + 0, (1, M, K), "bf16", std)
+    B = normal(s + 1, (1, N, K), "bf16", std)
+    C = normal(s + 2, (1, M, N), "bf16") if c else None
+    return Inputs("act_4096_bf16_gelu", M, N, K, 1, "bf16", "bf16", A, B, C=C,
+                  c_dt="bf16" if c else "none", d_dt="bf16", post_dt="bf16", alpha=1.0,
+                  beta=beta, act=act)
+
+
+def square_8192(dt="f16"):
+    """8192^3, U[-1, 1), K-major A and B, D in the input type."""
+    s = 1111 + 10 * 2
+    M = N = K = 8192
+    A = uniform(s + 0, (1, M, K), dt)
+    B = uniform(s + 1, (1, N, K), dt)
+    return Inputs(f"square_8192_{dt}", M, N, K, 1, dt, dt, A, B, d_dt=dt)
+
+
+def batched_2048():
+    """M = N = 2048, K = 4096, L = 16, fp16 U[-1,1), A M-major, B N-major, fp16 D."""
+    s = 1111 + 10 * 2 + 5
+    M = N = 2048
+    K = 4096
+    L = 16
+    A = make_a(uniform, L, M, K, True, s + 0, "f16")
+    B = make_b(uniform, L, N, K, True, s + 1, "f16")
+    return Inputs("batched_2048x2048x4096x16_f16_mn", M, N, K, L, "f16", "f16", A, B, d_dt="f16")
+
+
+def fp8_8192():
+    """8192^3, A e4m3 and B e5m2 (K-major) quantised from N(0,1) with per-tensor scales
+    amax/448 and amax/57344; alpha = s_a * s_b; bf16 D."""
+    s = 1111 + 10 * 3
+    M = N = K = 8192
+    A, sa = quantize_fp8(s + 0, (1, M, K), "e4m3")
+    B, sb = quantize_fp8(s + 1, (1, N, K), "e5m2")
+    alpha = float(np.float32(sa) * np.float32(sb))
+    return Inputs("fp8_8192_e4m3xe5m2", M, N, K, 1, "e4m3", "e5m2", A, B, d_dt="bf16",
+                  alpha=alpha, extra={"scale_a": sa, "scale_b": sb})
+
+
+def group_sizes(seed, G, unit=128, max_units=32):
+    return rng(seed).integers(1, max_units + 1, size=G) * unit
+
+
+def varlen_moe(G=8, N=4096, K=4096, sizes=None, std=1.0 / 64.0, act="silu"):
+    """Varlen-M: G groups, M_g = 128 * U{1..32}; A (sum M_g, K) bf16 ~ N(0,1)/64; B (G, N, K)
+    bf16 ~ N(0,1)/64; SiLU; PostAct only (bf16)."""
+    s = 1111 + 10 * 4
+    if sizes is None:
+        sizes = group_sizes(s + 3, G)
+    sizes = np.asarray(sizes, dtype=np.int64)
+    cu = np.zeros(G + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(sizes)
+    M = int(cu[-1])
+    A = normal(s + 0, (M, K), "bf16", std)
+    B = normal(s + 1, (G, N, K), "bf16", std)
+    return Inputs("varlen_m_8x4096x4096_bf16_silu", M, N, K, G, "bf16", "bf16", A, B,
+                  post_dt="bf16", act=act, cu_seqlens=cu)
+
+
+WORKLOADS = {
+    "plain_256": plain_256,
+    "act_4096": act_4096,
+    "square_8192_f16": lambda: square_8192("f16"),
+    "square_8192_bf16": lambda: square_8192("bf16"),
+    "batched_2048": batched_2048,
+    "fp8_8192": fp8_8192,
+    "varlen_moe": varlen_moe,
+}
