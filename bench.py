@@ -1,0 +1,180 @@
+"""Benchmark: GEMM TFLOP/s and fraction of the MFMA peak on one MI355X.
+
+Default workload: 8192^3 bf16 (A, B K-major, D bf16), one persistent-GEMM launch per step.
+Inputs are seeded synthetic data already resident in HBM when the timed region starts.
+Timing: HIP events on the stream the kernel is launched on (torch's current stream), around
+exactly --steps launches after --warmup untimed ones, bracketed by device synchronisation.
+The same line also reports the fp8 (e4m3 x e5m2) 8192^3 and varlen-M grouped workloads,
+the roofline of the dominant kernel and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOPS and % of MFMA peak at 8192^3 bf16/fp8; varlen-M grouped TFLOPS"
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "e5m2": 5000.0}
+HBM_PEAK_GBS = 8000.0
+PRIMARY = "square_8192_bf16"
+SECONDARY = ["fp8_8192", "varlen_moe", "square_8192_f16", "act_4096", "batched_2048"]
+
+
+def source_hash():
+    """Hash of the kernel sources: traffic counters are only reported for the same code."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_epilogue_persistent_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(inp):
+    """Minimum HBM bytes: read A, B (and C) once, write the outputs once."""
+    es = {"f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e5m2": 1, "none": 0}
+    if inp.varlen:
+        a = inp.M * inp.K * es[inp.a_dt]
+        b = inp.L * inp.N * inp.K * es[inp.b_dt]
+        mn = inp.M * inp.N
+    else:
+        a = inp.L * inp.M * inp.K * es[inp.a_dt]
+        b = inp.L * inp.N * inp.K * es[inp.b_dt]
+        mn = inp.L * inp.M * inp.N
+    return a + b + mn * (es[inp.c_dt] + es[inp.d_dt] + es[inp.post_dt])
+
+
+def setup(name):
+    import torch
+    import workloads as W
+    from gemm_epilogue_persistent_amd import Plan
+    from workloads import to_dev, out_like
+    inp = W.WORKLOADS[name]()
+    A, B, C = to_dev(inp.A), to_dev(inp.B), to_dev(inp.C)
+    D = out_like(inp, inp.d_dt) if inp.d_dt != "none" else None
+    P = out_like(inp, inp.post_dt) if inp.post_dt != "none" else None
+    cu = torch.from_numpy(inp.cu_seqlens).to("cuda") if inp.varlen else None
+    plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu)
+    args = (A, B, C, D, P, None, None, cu)
+    return inp, plan, args
+
+
+def time_plan(plan, args, steps, warmup):
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        plan.run(*args)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        plan.run(*args)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per launch
+
+
+def cpu_baseline(inp, budget_s=15.0):
+    """The oracle, as is, on whole output rows of the workload (bounded sample)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    prob = oracle.problem_from(inp)
+    codes = (W.codes_of(inp.A), W.codes_of(inp.B), W.codes_of(inp.C) if inp.C is not None else None)
+    # calibrate on one row per thread, then size the sample to the budget
+    rows = np.stack([np.zeros(cores, np.int64), np.arange(cores, dtype=np.int64) * 7 % inp.M], 1)
+    t0 = time.perf_counter()
+    prob.rows(*codes, rows, nthreads=cores)
+    t1 = time.perf_counter() - t0
+    nrows = max(cores, int(cores * budget_s / max(t1, 1e-3)) // cores * cores)
+    rows = np.stack([np.zeros(nrows, np.int64), (np.arange(nrows, dtype=np.int64) * 1031) % inp.M], 1)
+    t0 = time.perf_counter()
+    prob.rows(*codes, rows, nthreads=cores)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * nrows * inp.N * inp.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nrows} whole output rows of {inp.name} ({nrows * inp.N} outputs, "
+                      f"{flops / 1e9:.1f} GFLOP) in {dt:.1f} s, fp64 k-ascending dot products"}
+
+
+def traffic_for(name, launches_ms):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=PRIMARY)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the GEMM shards without communication; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    inp, plan, args = setup(a.workload)
+    tm, tn, G, xcd, T, P = plan.grid()
+    torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ms = time_plan(plan, args, a.steps, a.warmup)
+    flops = inp.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[inp.a_dt]
+    traffic = traffic_for(a.workload, ms)
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4), "traffic": traffic,
+            "kernel": "gemm_persistent_kernel", "algorithmic_bytes": algorithmic_bytes(inp),
+            "hbm_gbs_algorithmic": round(algorithmic_bytes(inp) / (ms * 1e-3) / 1e9, 1)}
+    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": inp.a_dt, "data": "synthetic",
+           "config": {"workload": inp.name, "M": inp.M, "N": inp.N, "K": inp.K, "L": inp.L,
+                      "tile": [tm, tn], "group_m": G, "xcd_remap": xcd, "tiles": T, "grid": P,
+                      "pct_of_peak": round(100 * tflops / peak, 2)},
+           "roofline": roof}
+    del args, plan
+    if not a.no_secondary:
+        sec = {}
+        for name in SECONDARY:
+            if name == a.workload:
+                continue
+            i2, p2, a2 = setup(name)
+            ms2 = time_plan(p2, a2, max(5, a.steps // 5), max(2, a.warmup // 2))
+            t2 = i2.flops() / (ms2 * 1e-3) / 1e12
+            sec[name] = {"tflops": round(t2, 2), "ms": round(ms2, 4),
+                         "pct_of_peak": round(100 * t2 / PEAK_TFLOPS[i2.a_dt], 2),
+                         "peak": PEAK_TFLOPS[i2.a_dt], "dtype": i2.a_dt}
+            del p2, a2, i2
+            torch.cuda.empty_cache()
+        out["secondary"] = sec
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, a.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

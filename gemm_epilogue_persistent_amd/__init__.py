@@ -1,0 +1,183 @@
+"""Python binding of the MI355X GEMM-with-epilogue library (argument marshalling only).
+
+    D       = alpha * A x B + beta * C
+    PostAct = act(alpha * A x B + beta * C)
+
+Every step runs in the HIP kernels of libgemm_mi355x.so, reached through its C ABI
+(include/gemm_mi355x.h); torch supplies device memory and the current stream. There is no
+fallback path: if the library is missing, importing the binding's entry points raises.
+
+Tensors follow the wrapper convention of quack-kernels (0.1.10 -> 0.2.0 diff, page 5,
+quack/dense_gemm_sm90.py, gemm_sm90): A (l, m, k), B (l, n, k), C / D / PostAct (l, m, n),
+with the major mode of each read from its strides; 2-D tensors mean l = 1. In varlen-M
+mode (cu_seqlens_m given) A is (M, K), B is (G, N, K), C / D / PostAct are (M, N).
+"""
+import ctypes
+
+import torch
+
+from . import _abi
+from ._abi import GemmError, DT, ACT, ROW, COL
+
+_TORCH_DT = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32",
+             torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}
+
+__all__ = ["Plan", "gemm", "gemm_create", "gemm_run", "plan_grid", "fastdivmod_params",
+           "fastdivmod_check", "GemmError", "library_path"]
+
+
+def library_path():
+    return _abi.LIB_PATH
+
+
+def _dt(t):
+    if t is None:
+        return "none"
+    try:
+        return _TORCH_DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _as3(t):
+    return None if t is None else (t if t.dim() == 3 else t.unsqueeze(0))
+
+
+def _major_ld(t, first_major_name):
+    """(major, ld) of a (.., X, Y) tensor: ROW if Y is contiguous, else COL if X is.
+    Zero-element tensors have no meaningful strides: they are described as packed rows."""
+    if t.numel() == 0:
+        return ROW, t.shape[-1]
+    if t.stride(-1) == 1 and (t.shape[-2] <= 1 or t.stride(-2) >= t.shape[-1] or t.stride(-2) != 1):
+        return ROW, (t.stride(-2) if t.shape[-2] > 1 else max(t.shape[-1], 1))
+    if t.stride(-2) == 1:
+        return COL, (t.stride(-1) if t.shape[-1] > 1 else max(t.shape[-2], 1))
+    raise ValueError(f"{first_major_name}: one of the last two dimensions must be contiguous")
+
+
+def _bstride(t):
+    return t.stride(0) if (t.dim() == 3 and t.shape[0] > 1 and t.numel() > 0) else 0
+
+
+def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none",
+             varlen=False, tile=None, group_m=0, max_ctas=0, xcd_remap=0):
+    """Build the gemm_desc for these tensors (no GPU work)."""
+    d = _abi.GemmDesc()
+    if varlen:
+        M, K = A.shape
+        G, N, K2 = B.shape
+        L = G
+        A3, B3 = A.unsqueeze(0), B
+        C3, D3, P3 = (None if x is None else x.unsqueeze(0) for x in (C, D, PostAct))
+    else:
+        A3, B3, C3, D3, P3 = (_as3(x) for x in (A, B, C, D, PostAct))
+        L, M, K = A3.shape
+        L2, N, K2 = B3.shape
+        if L2 != L:
+            raise ValueError("A and B batch counts differ")
+    if K2 != K:
+        raise ValueError("A and B disagree on K")
+    for name, x in (("C", C3), ("D", D3), ("PostAct", P3)):
+        if x is not None and tuple(x.shape[-2:]) != (M, N):
+            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected (.., {M}, {N})")
+    d.M, d.N, d.K, d.L = M, N, K, L
+    d.a, d.b, d.c, d.d, d.post = (DT[_dt(x)] for x in (A, B, C, D, PostAct))
+    d.a_major, d.lda = _major_ld(A3, "A")
+    d.b_major, d.ldb = _major_ld(B3, "B")
+    d.sa, d.sb = (0 if varlen else _bstride(A3)), _bstride(B3)
+    for x, mf, lf, sf in ((C3, "c_major", "ldc", "sc"), (D3, "d_major", "ldd", "sd"),
+                          (P3, "post_major", "ldp", "sp")):
+        if x is not None:
+            mj, ld = _major_ld(x, mf)
+            setattr(d, mf, mj)
+            setattr(d, lf, ld)
+            setattr(d, sf, 0 if varlen else _bstride(x))
+    d.alpha, d.beta = float(alpha), float(beta)
+    d.act = ACT[act]
+    d.varlen_m = int(varlen)
+    if tile is not None:
+        d.tile_m, d.tile_n = tile
+    d.group_m, d.max_ctas, d.xcd_remap = group_m, max_ctas, xcd_remap
+    return d
+
+
+def gemm_create(desc):
+    lib = _abi.load()
+    h = ctypes.c_void_p()
+    _abi.check(lib.gemm_create(ctypes.byref(desc), ctypes.byref(h)))
+    return h
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Plan:
+    """A validated plan for one problem shape (host memory; reusable across calls)."""
+
+    def __init__(self, A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none",
+                 cu_seqlens_m=None, **tuning):
+        self.varlen = cu_seqlens_m is not None
+        self.desc = describe(A, B, C, D, PostAct, alpha, beta, act, self.varlen, **tuning)
+        self.handle = gemm_create(self.desc)
+        self._lib = _abi.load()
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            self._lib.gemm_destroy(h)
+            self.handle = None
+
+    def run(self, A, B, C=None, D=None, PostAct=None, alpha_dev=None, beta_dev=None,
+            cu_seqlens_m=None, stream=None, tile_log=None, max_iters=0):
+        """Enqueue on `stream` (default: torch's current stream). alpha_dev / beta_dev:
+        optional fp32 device tensors of one element, read by the kernel."""
+        args = [self.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(PostAct), _ptr(alpha_dev),
+                _ptr(beta_dev), _ptr(cu_seqlens_m)]
+        if tile_log is not None:
+            st = self._lib.gemm_run_logged(*args, _ptr(tile_log), int(max_iters), _stream(stream))
+        else:
+            st = self._lib.gemm_run(*args, _stream(stream))
+        _abi.check(st)
+
+    def grid(self, num_cus=None):
+        """(tile_m, tile_n, group_m, xcd_remap, tiles, grid) for a device with num_cus CUs."""
+        if num_cus is None:
+            num_cus = torch.cuda.get_device_properties(0).multi_processor_count
+        out = [ctypes.c_int32() for _ in range(4)]
+        T = ctypes.c_int64()
+        P = ctypes.c_int32()
+        _abi.check(self._lib.gemm_plan_grid(self.handle, int(num_cus), *(ctypes.byref(o) for o in out),
+                                            ctypes.byref(T), ctypes.byref(P)))
+        return tuple(o.value for o in out) + (T.value, P.value)
+
+
+def gemm(A, B, D=None, C=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu_seqlens_m=None,
+         alpha_dev=None, beta_dev=None, stream=None, **tuning):
+    """One-shot call: plan (validated on the host) and enqueue. Outputs are written in place."""
+    p = Plan(A, B, C, D, PostAct, alpha, beta, act, cu_seqlens_m, **tuning)
+    p.run(A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, stream)
+    return D if D is not None else PostAct
+
+
+gemm_run = Plan.run
+plan_grid = Plan.grid
+
+
+def fastdivmod_params(d):
+    lib = _abi.load()
+    m = ctypes.c_uint32()
+    s = ctypes.c_uint32()
+    _abi.check(lib.gemm_fastdivmod_params(d, ctypes.byref(m), ctypes.byref(s)))
+    return m.value, s.value
+
+
+def fastdivmod_check(d_lo, d_hi, n_count, bad_dev, stream=None):
+    """Enqueue the device FastDivmod self-check; adds mismatches to bad_dev (uint64)."""
+    lib = _abi.load()
+    _abi.check(lib.gemm_fastdivmod_check(d_lo, d_hi, n_count, _ptr(bad_dev), _stream(stream)))

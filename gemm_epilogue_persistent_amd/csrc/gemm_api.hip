@@ -1,0 +1,125 @@
+// gemm_run / gemm_run_logged and the device FastDivmod self-check (C ABI).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/gemm_mi355x.h"
+#include "launch.hpp"
+
+namespace gep {
+gemm_status fail(gemm_status st, const char* fmt, ...);
+void clear_error();
+int32_t grid_size(const gemm_plan* p, int32_t num_cus);
+
+// Compute units of the current device, cached per device id.
+static gemm_status current_cus(int32_t* cus) {
+  static std::atomic<int32_t> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64) {
+    int32_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) { *cus = v; return GEMM_OK; }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || n <= 0) return fail(GEMM_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return GEMM_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
+                            void* Post, const float* alpha_dev, const float* beta_dev, const int32_t* cu,
+                            int32_t* tile_log, int32_t max_iters, void* stream) {
+  if (!plan) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: NULL plan");
+  // nothing to compute: no tiles (dense) or no rows / columns / groups (varlen)
+  const bool empty = plan->varlen ? (plan->base.M == 0 || plan->base.N == 0 || plan->L == 0) : plan->T == 0;
+  if (empty) { clear_error(); return GEMM_OK; }
+  if (plan->base.K > 0 && (!A || !B)) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: A and B are required");
+  if (plan->has_c != (C != nullptr)) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: C must be given iff the plan has a C type");
+  if (plan->has_d != (D != nullptr)) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: D must be given iff the plan has a D type");
+  if (plan->has_p != (Post != nullptr)) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: PostAct must be given iff the plan has a PostAct type");
+  if (plan->varlen && !cu) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: cu_seqlens_m is required for a varlen plan");
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D) || !aligned16(Post))
+    return fail(GEMM_ERR_ALIGNMENT, "gemm_run: operand pointers must be 16-byte aligned");
+  if (tile_log && max_iters <= 0) return fail(GEMM_ERR_INVALID_ARG, "gemm_run_logged: max_iters <= 0");
+
+  KParams k = plan->base;
+  k.A = plan->swapped ? B : A;
+  k.B = plan->swapped ? A : B;
+  k.C = C;
+  k.D = D;
+  k.Post = Post;
+  k.alpha_ptr = alpha_dev;
+  k.beta_ptr = beta_dev;
+  k.cu_seqlens = cu;
+  k.tile_log = tile_log;
+  k.tile_log_iters = tile_log ? max_iters : 0;
+  int32_t cus = 0;
+  gemm_status st = current_cus(&cus);
+  if (st != GEMM_OK) return st;
+  k.P = grid_size(plan, cus);
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (plan->key.op) {
+    case OP_F16: e = launch_f16(plan->key, k, s); break;
+    case OP_BF16: e = launch_bf16(plan->key, k, s); break;
+    default: e = launch_fp8(plan->key, k, s); break;
+  }
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  clear_error();
+  return GEMM_OK;
+}
+
+// For every divisor d in [d_lo, d_hi] (blocks, grid-stride) and dividend n < n_count
+// (threads), compare FastDivmod with the device's integer '/' and '%'.
+__global__ __launch_bounds__(256) void fastdivmod_check_kernel(uint32_t d_lo, uint32_t d_hi, uint32_t n_count,
+                                                               unsigned long long* bad) {
+  unsigned long long local = 0;
+  for (uint64_t d = (uint64_t)d_lo + blockIdx.x; d <= d_hi; d += gridDim.x) {
+    const FastDiv f = make_fastdiv((uint32_t)d);
+    for (uint64_t n = threadIdx.x; n < n_count; n += blockDim.x) {
+      uint32_t q, r;
+      fd_divmod(f, (uint32_t)n, q, r);
+      local += (q != (uint32_t)n / (uint32_t)d) | (r != (uint32_t)n % (uint32_t)d);
+    }
+  }
+  if (local) atomicAdd(bad, local);
+}
+
+}  // namespace gep
+
+extern "C" {
+
+gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D, void* PostAct,
+                     const float* alpha_dev, const float* beta_dev, const int32_t* cu_seqlens_m, void* stream) {
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, 0, stream);
+}
+
+gemm_status gemm_run_logged(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
+                            void* PostAct, const float* alpha_dev, const float* beta_dev,
+                            const int32_t* cu_seqlens_m, int32_t* tile_log, int32_t max_iters, void* stream) {
+  if (!tile_log) return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_logged: NULL tile_log");
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, tile_log, max_iters, stream);
+}
+
+gemm_status gemm_fastdivmod_check(uint32_t d_lo, uint32_t d_hi, uint32_t n_count, unsigned long long* bad_dev,
+                                  void* stream) {
+  if (!bad_dev || d_lo < 1 || d_lo > d_hi || d_hi > 0x7FFFFFFFu || n_count > 0x80000000u)
+    return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_fastdivmod_check: bad range or NULL counter");
+  uint64_t span = (uint64_t)d_hi - d_lo + 1;
+  unsigned blocks = (unsigned)(span < 65536 ? span : 65536);
+  hipLaunchKernelGGL(gep::fastdivmod_check_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, d_lo, d_hi,
+                     n_count, bad_dev);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return gep::fail(GEMM_ERR_HIP, "fastdivmod check launch: %s", hipGetErrorString(e));
+  gep::clear_error();
+  return GEMM_OK;
+}
+
+}  // extern "C"

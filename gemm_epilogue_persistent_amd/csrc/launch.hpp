@@ -1,0 +1,32 @@
+// Kernel entry points and the launcher table shared by the instantiation units.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "gemm_kernel.hpp"
+
+namespace gep {
+
+constexpr int kStages = 2;
+
+// Workgroups per CU the kernel is built for: 256x256 tiles hold 128 KB of LDS (one per CU),
+// 128x128 tiles 64 KB (two per CU).
+template <int BM>
+constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
+
+template <int BM, int OP, int FA, int FB, bool AK, bool BK, bool VL>
+__global__ __launch_bounds__(256, wg_per_cu<BM>()) void gemm_persistent_kernel(const KParams p) {
+  GemmKernel<BM, BM, OP, FA, FB, AK, BK, VL, kStages>::run(p);
+}
+
+template <int BM, int OP, int FA, int FB, bool AK, bool BK, bool VL>
+hipError_t launch_one(const KParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_persistent_kernel<BM, OP, FA, FB, AK, BK, VL>), dim3(p.P), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// One unit per op family; each returns hipErrorInvalidValue for a key it does not hold.
+hipError_t launch_f16(const KernelKey& k, const KParams& p, hipStream_t s);
+hipError_t launch_bf16(const KernelKey& k, const KParams& p, hipStream_t s);
+hipError_t launch_fp8(const KernelKey& k, const KParams& p, hipStream_t s);
+
+}  // namespace gep

@@ -122,16 +122,19 @@ typedef struct gemm_plan gemm_plan;
 
 /* Validate `desc` and build a plan (host memory only, no HIP call). On success *out owns a
  * new plan to release with gemm_destroy; on failure *out is set to NULL and the status
- * says why: INVALID_ARG (NULL desc/out, M/N/L <= 0, K < 0, strides smaller than the
+ * says why: INVALID_ARG (NULL desc/out, a negative size, strides smaller than the
  * extents they skip, unknown enum value), UNSUPPORTED (dtype or major combination the
  * pages exclude or this library does not build, tile pair not offered, tile count >= 2^31,
  * a tile's operand byte offsets >= 2^31), ALIGNMENT (contiguous extent or stride not a
- * multiple of 16 bytes), NO_MEMORY. K == 0 is valid: the product is then zero
- * (page 5, GemmSm90.mma sets the accumulator to zero when there is no k-tile). */
+ * multiple of 16 bytes), NO_MEMORY. Zero sizes are valid: M, N or L == 0 is an empty
+ * problem, and K == 0 makes the product zero (page 5, GemmSm90.mma sets the accumulator
+ * to zero when there is no k-tile). */
 gemm_status gemm_create(const gemm_desc* desc, gemm_plan** out);
 
 /* Enqueue the GEMM on `stream`. A, B, D / PostAct (those the plan declares present) must
- * be non-NULL device pointers; C must be non-NULL iff the plan has a C type.
+ * be non-NULL device pointers (A and B may be NULL when K == 0: they are not read);
+ * C must be non-NULL iff the plan has a C type. A plan with no output element (M, N or L
+ * zero) returns GEMM_OK without launching anything.
  * alpha_dev / beta_dev: optional device pointers to one fp32 each; when non-NULL they
  * replace desc.alpha / desc.beta and are read by the kernel at run time (page 5,
  * gemm_sm90 passes a tensor alpha/beta to the kernel as a pointer).

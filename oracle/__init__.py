@@ -195,6 +195,34 @@ class Problem:
         return pre, post
 
 
+def problem_from(inp, act=None, alpha=None, beta=None):
+    """Problem for a workload description (duck-typed: M, N, K, a_dt, b_dt, A, B, C, c_dt,
+    alpha, beta, act, cu_seqlens, with A / B / C torch views whose strides give the layout)."""
+    A, B = inp.A, inp.B
+    varlen = inp.cu_seqlens is not None
+    if varlen:
+        a_k = A.stride(1) == 1
+        lda = A.stride(0) if a_k else A.stride(1)
+        sa, L = 0, B.shape[0]
+    else:
+        a_k = A.stride(2) == 1
+        lda = A.stride(1) if a_k else A.stride(2)
+        sa, L = A.stride(0), A.shape[0]
+    b_k = B.stride(2) == 1
+    ldb = B.stride(1) if b_k else B.stride(2)
+    kw = {}
+    if inp.C is not None:
+        C = inp.C if inp.C.dim() == 3 else inp.C.unsqueeze(0)
+        c_n = C.stride(2) == 1
+        kw = dict(c_dt=inp.c_dt, c_nmajor=c_n, ldc=C.stride(1) if c_n else C.stride(2),
+                  sc=0 if varlen else C.stride(0))
+    return Problem(inp.M, inp.N, inp.K, L, inp.a_dt, inp.b_dt, a_kmajor=a_k, b_kmajor=b_k,
+                   lda=lda, ldb=ldb, sa=sa, sb=B.stride(0),
+                   alpha=inp.alpha if alpha is None else alpha,
+                   beta=inp.beta if beta is None else beta,
+                   act=inp.act if act is None else act, cu_seqlens=inp.cu_seqlens, **kw)
+
+
 # ---------------------------------------------------------------------------------------
 # tile map and fast divmod
 # ---------------------------------------------------------------------------------------

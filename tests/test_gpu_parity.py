@@ -1,0 +1,320 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Small cases span several tiles and ragged tails in M, N and K and cover every dtype, major
+mode, output type, activation, alpha/beta form, batch and varlen layout. Small-integer
+cases must match exactly. The five workloads run at full size with sampled outputs.
+The persistent schedule (device tile log) and the device FastDivmod are checked bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import (check_close, gather, oracle_codes, out_like, problem_of, run_hip,
+                    sample_points, to_dev, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(name):
+    print(f"[case] {name}", flush=True)
+    sys.stdout.flush()
+
+
+def small(M, N, K, L, a_dt, b_dt=None, a_mmaj=False, b_nmaj=False, c_dt="none", d_dt="bf16",
+          post_dt="none", act="none", alpha=1.0, beta=1.0, seed=0, gen=W.uniform, c_mmaj=False):
+    b_dt = b_dt or a_dt
+    A = W.make_a(gen, L, M, K, a_mmaj, 500 + seed, a_dt)
+    B = W.make_b(gen, L, N, K, b_nmaj, 600 + seed, b_dt)
+    C = None
+    if c_dt != "none":
+        C = gen(700 + seed, (L, N, M), c_dt).permute(0, 2, 1) if c_mmaj else gen(700 + seed, (L, M, N), c_dt)
+    return W.Inputs(f"small_{a_dt}", M, N, K, L, a_dt, b_dt, A, B, C=C, c_dt=c_dt, d_dt=d_dt,
+                    post_dt=post_dt, alpha=alpha, beta=beta, act=act)
+
+
+def compare_full(inp, tile=None, d_major_m=False, **kw):
+    announce(f"{inp.name} M={inp.M} N={inp.N} K={inp.K} L={inp.L} tile={tile} mmaj_out={d_major_m}")
+    d, p, _ = run_hip(inp, d_major_m=d_major_m, tile=tile, **kw)
+    pre, post = problem_of(inp).all(*oracle_codes(inp))
+    tol, rms = tol_for(inp)
+    if d is not None:
+        check_close(d, pre, tol, rms, "D")
+    if p is not None:
+        check_close(p, post, tol, rms, "PostAct")
+    return d, p, pre, post
+
+
+# ---------------------------------------------------------------------------------------
+# small shapes: every dtype / major / tile, ragged tails
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("a_mmaj,b_nmaj", [(False, False), (True, False), (False, True), (True, True)])
+def test_small_16bit_majors(tile, dt, a_mmaj, b_nmaj):
+    inp = small(296, 392, 200, 1, dt, a_mmaj=a_mmaj, b_nmaj=b_nmaj, d_dt=dt, seed=1)
+    compare_full(inp, tile=tile)
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e5m2"), ("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e5m2", "e4m3")])
+def test_small_fp8(tile, fa, fb):
+    inp = small(264, 200, 336, 1, fa, fb, d_dt="bf16", seed=2, alpha=0.5)
+    compare_full(inp, tile=tile)
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+@pytest.mark.parametrize("act", ["none", "relu", "relu_sq", "gelu_tanh", "silu"])
+def test_small_epilogue_acts(tile, act):
+    inp = small(136, 520, 96, 1, "bf16", c_dt="bf16", d_dt="bf16", post_dt="bf16", act=act,
+                alpha=1.5, beta=0.5, seed=3, gen=lambda s, sh, dt: W.normal(s, sh, dt, 0.5))
+    compare_full(inp, tile=tile)
+
+
+@pytest.mark.parametrize("c_dt,d_dt,post_dt", [("f32", "f32", "none"), ("f16", "none", "f16"),
+                                               ("none", "f32", "bf16"), ("bf16", "f16", "f32")])
+def test_small_output_types(c_dt, d_dt, post_dt):
+    act = "gelu_tanh" if post_dt != "none" else "none"
+    inp = small(200, 264, 64, 1, "f16", c_dt=c_dt, d_dt=d_dt, post_dt=post_dt, act=act,
+                alpha=-0.75, beta=2.0, seed=4)
+    compare_full(inp)
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_small_batched_strided(tile):
+    inp = small(160, 136, 72, 3, "bf16", a_mmaj=True, c_dt="f32", d_dt="bf16", beta=-1.0, seed=5)
+    compare_full(inp, tile=tile)
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_small_m_major_outputs(tile):
+    # C, D, PostAct all M-contiguous (computed as the transposed problem)
+    inp = small(264, 136, 80, 2, "f16", b_nmaj=True, c_dt="f16", d_dt="f16", post_dt="bf16",
+                act="relu", beta=0.25, seed=6, c_mmaj=True)
+    compare_full(inp, tile=tile, d_major_m=True)
+
+
+def test_k_zero_and_empty():
+    inp = small(130, 136, 0, 2, "bf16", c_dt="f32", d_dt="f32", beta=0.5, seed=7)
+    inp.A = torch.zeros((2, 130, 0), dtype=torch.bfloat16)
+    inp.B = torch.zeros((2, 136, 0), dtype=torch.bfloat16)
+    d, _, _ = run_hip(inp)
+    assert np.array_equal(d, 0.5 * inp.C.double().numpy())
+    # M = 0: nothing to do, no launch
+    e = small(0, 64, 64, 1, "bf16", seed=8)
+    d, _, _ = run_hip(e)
+    assert d.shape == (1, 0, 64)
+
+
+def test_alpha_beta_device_pointers():
+    inp = small(256, 256, 128, 1, "bf16", c_dt="bf16", d_dt="f32", alpha=99.0, beta=99.0, seed=9)
+    a = torch.tensor([0.25], dtype=torch.float32, device="cuda")
+    b = torch.tensor([-2.0], dtype=torch.float32, device="cuda")
+    d, _, _ = run_hip(inp, alpha_dev=a, beta_dev=b)
+    pre, _ = problem_of(inp, alpha=0.25, beta=-2.0).all(*oracle_codes(inp))
+    check_close(d, pre, 1e-5, 1e-5, "D")
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "e4m3", "e5m2"])
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_small_integers_exact(dt, tile):
+    """Entries in {-3..3}: products and fp32 sums are exact, so f32 D equals the oracle."""
+    r = np.random.Generator(np.random.PCG64(11))
+    M, N, K = 200, 264, 512
+    a = r.integers(-3, 4, size=(1, M, K)).astype(np.float64)
+    b = r.integers(-3, 4, size=(1, N, K)).astype(np.float64)
+    c = r.integers(-8, 9, size=(1, M, N)).astype(np.float64)
+    inp = W.Inputs("ints", M, N, K, 1, dt, dt, W.to_dtype(a, dt), W.to_dtype(b, dt),
+                   C=W.to_dtype(c, "f32"), c_dt="f32", d_dt="f32", beta=2.0)
+    d, _, _ = run_hip(inp, tile=tile)
+    exact = np.einsum("lmk,lnk->lmn", a, b) + 2.0 * c
+    assert np.array_equal(d, exact)
+    pre, _ = problem_of(inp).all(*oracle_codes(inp))
+    assert np.array_equal(d, pre)
+
+
+def test_identity_exact():
+    K = 256
+    eye = torch.eye(K, dtype=torch.float64).to(torch.bfloat16).reshape(1, K, K)
+    B = W.uniform(12, (1, 384, K), "bf16")
+    inp = W.Inputs("id", K, 384, K, 1, "bf16", "bf16", eye, B, d_dt="bf16")
+    d, _, _ = run_hip(inp)
+    assert np.array_equal(d[0], B[0].double().numpy().T)
+
+
+# ---------------------------------------------------------------------------------------
+# varlen-M
+# ---------------------------------------------------------------------------------------
+
+def varlen_small(sizes, N=264, K=136, seed=13, act="silu", c=True, a_mmaj=False, dt="bf16"):
+    sizes = np.asarray(sizes)
+    cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    G, M = len(sizes), int(cu[-1])
+    if a_mmaj:
+        A = W.normal(800 + seed, (K, M), dt, 0.5).t()
+    else:
+        A = W.normal(800 + seed, (M, K), dt, 0.5)
+    B = W.normal(900 + seed, (G, N, K), dt, 0.5)
+    C = W.normal(1000 + seed, (M, N), "f32") if c else None
+    return W.Inputs("varlen_small", M, N, K, G, dt, dt, A, B, C=C, c_dt="f32" if c else "none",
+                    d_dt="bf16", post_dt="bf16", act=act, beta=0.5, cu_seqlens=cu)
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+@pytest.mark.parametrize("sizes", [[0, 300, 0, 1, 129, 0], [256, 256, 256], [5], [0, 0, 77],
+                                   [384, 0, 513, 128, 1, 255]])
+def test_varlen_small(tile, sizes):
+    compare_full(varlen_small(sizes), tile=tile)
+
+
+def test_varlen_m_major_a_and_fp8():
+    compare_full(varlen_small([136, 0, 264, 16], a_mmaj=True, dt="f16"))
+    sizes = np.array([64, 0, 200, 128])
+    cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, N, K, G = int(cu[-1]), 136, 256, 4
+    A, sa = W.quantize_fp8(31, (M, K), "e4m3")
+    B, sb = W.quantize_fp8(32, (G, N, K), "e5m2")
+    inp = W.Inputs("varlen_fp8", M, N, K, G, "e4m3", "e5m2", A, B, d_dt="bf16", alpha=sa * sb,
+                   cu_seqlens=cu)
+    compare_full(inp)
+
+
+def test_varlen_all_groups_empty():
+    inp = varlen_small([0, 0, 0])
+    d, p, _ = run_hip(inp)
+    assert d.shape == (0, 264)
+
+
+# ---------------------------------------------------------------------------------------
+# persistent schedule and FastDivmod, bit for bit
+# ---------------------------------------------------------------------------------------
+
+def device_schedule(inp, P, max_iters, **tuning):
+    log = torch.full((P * max_iters * 4,), -1, dtype=torch.int32, device="cuda")
+    run_hip(inp, tile_log=log, max_iters=max_iters, **tuning)
+    return log.view(P, max_iters, 4).cpu().numpy()
+
+
+@pytest.mark.parametrize("M,N,L,G,xcd,tile", [(2560, 2176, 2, 8, 0, (256, 256)),
+                                              (2560, 2176, 1, 4, 1, (128, 128)),
+                                              (1280, 4224, 3, 16, 0, (128, 128)),
+                                              (5000 - 8, 512, 1, 1, 0, (256, 256))])
+def test_tile_schedule_dense(M, N, L, G, xcd, tile):
+    inp = small(M, N, 16, L, "bf16", d_dt="bf16", seed=14)
+    tm, tn = -(-M // tile[0]), -(-N // tile[1])
+    T = tm * tn * L
+    plan_args = dict(tile=tile, group_m=G, xcd_remap=1 if xcd else -1)
+    _, _, plan = run_hip(inp, **plan_args)
+    _, _, Gp, xr, Tp, P = plan.grid()
+    assert (Gp, Tp, xr) == (G, T, 1 if xcd else 0)
+    max_iters = -(-T // P) + 1
+    log = device_schedule(inp, P, max_iters, **plan_args)
+    want = oracle.tile_schedule(P, T, lambda t: oracle.tile_dense(t, tm, tn, G), bool(xcd))
+    for b in range(P):
+        seq = want[b]
+        got = log[b]
+        assert [tuple(x[:3]) for x in got[:len(seq)]] == [tuple(s) for s in seq], b
+        assert (got[len(seq):] == -1).all()
+        assert [x[3] for x in got[:len(seq)]] == [oracle.wg_tile(b, i, P, bool(xcd)) for i in range(len(seq))]
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_tile_schedule_varlen(tile):
+    inp = varlen_small([0, 300, 0, 1, 129, 0, 700, 256], N=520, K=16)
+    cu = inp.cu_seqlens
+    tn = -(-inp.N // tile[1])
+    T = oracle.tile_count_varlen(cu, tile[0], tile[1], inp.N)
+    _, _, plan = run_hip(inp, tile=tile, group_m=2)
+    P = plan.grid()[5]
+    max_iters = -(-T // P) + 1
+    log = device_schedule(inp, P, max_iters, tile=tile, group_m=2)
+    want = oracle.tile_schedule(P, T, lambda t: oracle.tile_varlen(t, cu, tile[0], tn, 2), True)
+    for b in range(P):
+        seq = want[b]
+        assert [tuple(x[:3]) for x in log[b][:len(seq)]] == [tuple(s) for s in seq], b
+        assert (log[b][len(seq):] == -1).all()
+
+
+def test_fastdivmod_device_exhaustive_below_2_16():
+    from gemm_epilogue_persistent_amd import fastdivmod_check
+    bad = torch.zeros(1, dtype=torch.int64, device="cuda")
+    fastdivmod_check(1, 1 << 16, 1 << 16, bad)
+    # the largest divisors with every dividend in [0, 2^31)
+    fastdivmod_check((1 << 31) - 16, (1 << 31) - 1, 1 << 31, bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+
+
+# ---------------------------------------------------------------------------------------
+# the five workloads at full size (sampled outputs) and the guards that isolate the GEMM
+# ---------------------------------------------------------------------------------------
+
+def full_size(inp, npts=3000, rows=2, seed=0, **kw):
+    announce(f"{inp.name} full size")
+    d, p, _ = run_hip(inp, **kw)
+    prob = problem_of(inp)
+    codes = oracle_codes(inp)
+    pts = sample_points(inp, npts, seed)
+    pre, post = prob.points(*codes, pts)
+    tol, rms = tol_for(inp)
+    if d is not None:
+        check_close(gather(d, pts, inp.varlen), pre, tol, rms, "D sampled")
+    if p is not None:
+        check_close(gather(p, pts, inp.varlen), post, tol, rms, "PostAct sampled")
+    # whole rows (every column of a few rows, across all N-tiles)
+    r = np.random.Generator(np.random.PCG64(seed + 1))
+    L = 1 if inp.varlen else inp.L
+    rr = np.stack([r.integers(0, L, rows), r.integers(0, inp.M, rows)], 1)
+    rpre, rpost = prob.rows(*codes, rr)
+    for i, (l, m) in enumerate(rr):
+        if d is not None:
+            check_close(d[m] if inp.varlen else d[l, m], rpre[i], tol, rms, "D row")
+        if p is not None:
+            check_close(p[m] if inp.varlen else p[l, m], rpost[i], tol, rms, "PostAct row")
+    # every output element was written
+    for x in (d, p):
+        if x is not None:
+            assert np.isfinite(x).all()
+    return d, p
+
+
+def test_workload_plain_256_full():
+    compare_full(W.plain_256())
+
+
+def test_workload_act_4096():
+    full_size(W.act_4096())
+
+
+def test_workload_act_4096_gemm_only_guard():
+    # beta = 0 and no activation: the GEMM term alone must match
+    full_size(W.act_4096(beta=0.0, act="none"))
+
+
+def test_workload_square_8192_f16():
+    full_size(W.square_8192("f16"), npts=1500, rows=1)
+
+
+def test_workload_square_8192_bf16():
+    full_size(W.square_8192("bf16"), npts=1500, rows=1)
+
+
+def test_workload_batched_2048():
+    full_size(W.batched_2048(), npts=2000, rows=2)
+
+
+def test_workload_fp8_8192():
+    full_size(W.fp8_8192(), npts=1500, rows=1)
+
+
+def test_workload_varlen_moe():
+    full_size(W.varlen_moe(), npts=3000, rows=2)
+
+
+def test_workload_varlen_moe_unscaled_guard():
+    # N(0,1) inputs: SiLU of O(64) values, far from the all-zero output
+    full_size(W.varlen_moe(std=1.0), npts=2000, rows=1)

@@ -211,3 +211,32 @@ WORKLOADS = {
     "fp8_8192": fp8_8192,
     "varlen_moe": varlen_moe,
 }
+
+
+# ---------------------------------------------------------------------------------------
+# device placement (layout-preserving copies and output buffers)
+# ---------------------------------------------------------------------------------------
+
+def to_dev(t):
+    """Copy a (possibly permuted) CPU view to the GPU with the same strides."""
+    if t is None:
+        return None
+    base = t
+    while base._base is not None:
+        base = base._base
+    dbase = base.to("cuda")
+    return torch.as_strided(dbase, t.size(), t.stride(), t.storage_offset())
+
+
+def out_like(inp, dt, m_major=False, fill=float("nan")):
+    """Output (L, M, N) (varlen: (M, N)) of type dt on the GPU, N- or M-contiguous,
+    pre-filled with `fill` so that unwritten elements show."""
+    tdt = TORCH_DT[dt]
+    if inp.varlen:
+        t = torch.empty((inp.N, inp.M), dtype=tdt, device="cuda").t() if m_major else \
+            torch.empty((inp.M, inp.N), dtype=tdt, device="cuda")
+    else:
+        t = torch.empty((inp.L, inp.N, inp.M), dtype=tdt, device="cuda").permute(0, 2, 1) if m_major \
+            else torch.empty((inp.L, inp.M, inp.N), dtype=tdt, device="cuda")
+    t.fill_(fill)
+    return t
