@@ -8,19 +8,24 @@
 //   * 256 threads = 4 wave64s in a 2x2 grid; each wave owns a (BM/2) x (BN/2) block of the
 //     output tile, computed with v_mfma_f32_32x32x16_{f16,bf16} or, for fp8,
 //     v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales; per-operand e4m3/e5m2 format fields).
-//   * A and B k-tiles of 128 bytes per row travel global -> LDS with buffer_load ... lds
-//     (no VGPR staging), STAGES deep. Out-of-range rows / k-chunks use an offset past the
-//     buffer's num_records, which the hardware reads as zero (tails in M, N and K).
-//   * K-major tiles are stored [row][8 x 16-byte chunks] with the chunk index XOR-swizzled
+//   * A and B k-tiles of 64 bytes per row travel global -> LDS with buffer_load ... lds
+//     (no VGPR staging) into a STAGES-deep ring, issued STAGES-1 k-tiles ahead.
+//     Out-of-range rows / k-chunks use an offset past the buffer's num_records, which the
+//     hardware reads as zero (tails in M, N and K).
+//   * K-major tiles are stored [row][4 x 16-byte chunks] with the chunk index XOR-swizzled
 //     by the row, so the 32-row MFMA fragment reads (ds_read_b128) hit distinct banks.
 //     M/N-major (16-bit) tiles are stored [k][row] and read with ds_read_b64_tr_b16, which
 //     transposes 16x4 blocks across each 16-lane group into K-contiguous fragments.
+//   * Fragments are double-buffered in registers: the LDS reads of the next k-step are
+//     interleaved with the MFMAs of the current one. The once-per-k-tile barrier sits before
+//     the last k-step's MFMAs, so the next k-tile's first fragments load under them.
 //   * Persistent grid: workgroup b takes tiles t = b' + i*P; t -> (m_blk, n_blk, l) by the
 //     grouped raster with FastDivmod (page 6, quack/fast_math.py); b' optionally remaps b so
 //     that the workgroups of one XCD (dispatched round-robin) take consecutive tile ids.
-//   * Epilogue straight from the accumulators: the MFMA is issued as (B fragment,
-//     A fragment) so each lane holds 4 consecutive N values of one row, which it scales,
-//     adds beta*C to, activates and stores as 8- or 16-byte vectors.
+//   * Epilogue: the accumulators go, 16 rows at a time, through one stage-sized region of
+//     the ring as fp32 and come back row-contiguous (4 columns per lane) for scaling,
+//     beta*C, the activation, conversion and coalesced stores. The next tile's first k-tile
+//     loads are already in flight in the other stages meanwhile.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -41,8 +46,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------------------------
 // MFMA flavours. Frag = the per-lane operand registers of one 32-row fragment.
-// Lane l holds row (l % 32) and, inside the MFMA's K slice, elements [8*(l/32), +8) for
-// 16-bit types or bytes [32*(l/32), +32) for fp8; A and B use the same K assignment.
+// Lane l holds row (l % 32) and, inside the instruction's K slice, elements [8*(l/32), +8)
+// for 16-bit types or bytes [32*(l/32), +32) for fp8; A and B use the same K assignment.
+// The kernel passes the B fragment as the instruction's first source and the A fragment as
+// its second, so that each output lane holds 4 consecutive N values (see the epilogue).
 // ------------------------------------------------------------------------------------
 template <int OP, int FA, int FB>
 struct Mfma;
@@ -74,10 +81,8 @@ struct Mfma<OP_FP8, FA, FB> {
   static constexpr int kES = 1;
   static constexpr int kKStep = 64;
   using Frag = i32x8;
-  // cbsz / blgp select the format of the instruction's first / second source
-  // (0 = e4m3, 1 = e5m2). The kernel passes the B fragment first (see the epilogue
-  // layout note), so B's format goes in cbsz and A's in blgp.
-  // Scales of 127 are 2^0 in the E8M0 scale encoding (no scaling).
+  // cbsz / blgp select the format of the first / second source (0 = e4m3, 1 = e5m2):
+  // B's format goes in cbsz and A's in blgp. Scales of 127 are 2^0 in E8M0 (no scaling).
   static __device__ __forceinline__ f32x16 mma(Frag b, Frag a, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, 0, 127, 0, 127);
   }
@@ -86,11 +91,13 @@ struct Mfma<OP_FP8, FA, FB> {
 // ------------------------------------------------------------------------------------
 // LDS tile layouts
 // ------------------------------------------------------------------------------------
-constexpr int kRowBytes = 128;  // one k-tile row of a K-major tile
+constexpr int kRowBytes = 64;  // bytes of K per row of a K-major k-tile
+constexpr int kChunks = kRowBytes / 16;
 
-// K-major: chunk (16 bytes) c of row r lives at chunk c ^ swz(r). Rows r..r+15 of one
-// fragment read then cover all banks for both 8-lane (128 B) and 16-lane (256 B) phases.
-__device__ __forceinline__ int kswz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+// K-major: 16-byte chunk c of row r lives at chunk c ^ kswz(r). For any 16 consecutive rows
+// at one logical chunk, the 8-lane (128-byte) and 16-lane (256-byte) phases of a
+// ds_read_b128 then touch distinct bank groups.
+__device__ __forceinline__ int kswz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 // M/N-major: chunk c of k-row k lives at chunk c ^ mswz(k); the 4 k-rows that one 16-lane
 // transpose group reads land in 4 disjoint 64-byte bank ranges.
 __device__ __forceinline__ int mswz(int k) { return (k & 3) << 2; }
@@ -101,17 +108,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// Loader of one operand's k-tile: ROWS rows (M or N) by 128 bytes of K.
+// Loader of one operand's k-tile: ROWS rows (M or N) by kRowBytes of K.
 // Each wave issues kInstr instructions of 64 lanes x 16 bytes (1 KB of LDS each).
 template <int ROWS, bool KMAJ, int ES>
 struct TileLoader {
   static constexpr int kTileBytes = ROWS * kRowBytes;
   static constexpr int kInstr = kTileBytes / 1024 / 4;
-  static constexpr int kCPR = ROWS * ES / 16;          // MN-major: chunks per k-row
-  static constexpr int kKPI = KMAJ ? 1 : 1024 / (ROWS * ES);  // MN-major: k-rows per instruction
-  uint32_t off[kInstr];
-  int32_t kidx[kInstr];   // K-major: element k of the chunk; MN-major: the k-row
-  bool ok[kInstr];        // row (K-major) / column chunk (MN-major) inside the operand
+  static constexpr int kCPR = ROWS * ES / 16;                  // MN-major: chunks per k-row
+  static constexpr int kKPI = KMAJ ? 1 : 1024 / (ROWS * ES);   // MN-major: k-rows per instruction
+  static_assert(kInstr >= 1, "tile too small for 4 waves");
+  uint32_t off[kInstr];    // byte offset of this lane's chunk inside the k-tile
+  uint32_t offv[kInstr];   // off, or kOOB when the row / column chunk lies outside the operand
+  int32_t kidx[kInstr];    // K-major: element k of the chunk; MN-major: the k-row
 
   // rows_valid: rows of this tile that exist (K-major) or MN elements that exist (MN-major).
   __device__ __forceinline__ void init(int wave, int lane, int rows_valid, int64_t ld_bytes) {
@@ -119,33 +127,45 @@ struct TileLoader {
     for (int q = 0; q < kInstr; ++q) {
       const int blk = q * 4 + wave;
       if constexpr (KMAJ) {
-        const int row = blk * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ kswz(row);
+        const int row = blk * (1024 / kRowBytes) + lane / kChunks;
+        const int c = (lane % kChunks) ^ kswz(row);
         off[q] = (uint32_t)(row * ld_bytes + c * 16);
         kidx[q] = c * (16 / ES);
-        ok[q] = row < rows_valid;
+        offv[q] = row < rows_valid ? off[q] : kOOB;
       } else {
         const int krow = blk * kKPI + lane / kCPR;
         const int c = (lane % kCPR) ^ mswz(krow);
         off[q] = (uint32_t)(krow * ld_bytes + c * 16);
         kidx[q] = krow;
-        ok[q] = c * (16 / ES) < rows_valid;
+        offv[q] = c * (16 / ES) < rows_valid ? off[q] : kOOB;
       }
     }
   }
 
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, GEP_LDS char* lds, int wave, int k0,
-                                        int K) const {
+  // `tail`: this k-tile reaches past K, so chunks at k >= K must read as zero too.
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, GEP_LDS char* lds, int wave, int k0, int K,
+                                        bool tail) const {
+    if (!tail) {
 #pragma unroll
-    for (int q = 0; q < kInstr; ++q) {
-      const uint32_t o = (ok[q] && k0 + kidx[q] < K) ? off[q] : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GEP_LDS void*)(lds + (q * 4 + wave) * 1024), 16, o, 0, 0,
-                                               0);
+      for (int q = 0; q < kInstr; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GEP_LDS void*)(lds + (q * 4 + wave) * 1024), 16, offv[q],
+                                                 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kInstr; ++q) {
+        const uint32_t o = k0 + kidx[q] < K ? offv[q] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GEP_LDS void*)(lds + (q * 4 + wave) * 1024), 16, o, 0, 0,
+                                                 0);
+      }
     }
   }
 };
 
-// Fragment reader: rows [r0, r0+32) of a tile, MFMA k-step s (16-bit: 32 bytes; fp8: 64).
+// LDS reads per fragment (for the scheduling pattern).
+template <bool KMAJ, int ES>
+constexpr int reads_per_frag() { return KMAJ ? (ES == 2 ? 1 : 2) : 2; }
+
+// Fragment reader: rows [r0, r0+32) of a tile, MFMA k-step s of the k-tile.
 template <bool KMAJ, int ROWS, class Op>
 __device__ __forceinline__ typename Op::Frag read_frag(const GEP_LDS char* tile, int r0, int s, int lane) {
   using Frag = typename Op::Frag;
@@ -157,7 +177,7 @@ __device__ __forceinline__ typename Op::Frag read_frag(const GEP_LDS char* tile,
       const int c = s * 2 + (lane >> 5);
       return *(const GEP_LDS i32x4*)(rp + ((c ^ sw) << 4));
     } else {
-      const int c = s * 4 + (lane >> 5) * 2;
+      const int c = (lane >> 5) * 2;  // one fp8 k-step spans the whole 64-byte row
       i32x4 lo = *(const GEP_LDS i32x4*)(rp + ((c ^ sw) << 4));
       i32x4 hi = *(const GEP_LDS i32x4*)(rp + (((c + 1) ^ sw) << 4));
       return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -276,6 +296,15 @@ __device__ __forceinline__ void raster(const KParams& p, uint32_t r, uint32_t tm
   }
 }
 
+// Everything the loop needs about one output tile.
+struct TileInfo {
+  int l, m0, n0, row_end;
+  int mb, nb;          // block coordinates inside the batch / group
+  const char* a_tile;  // first byte of the tile's A rows (K-major) / columns (M-major)
+  const char* b_tile;
+  int64_t a_room, b_room;  // bytes from the tile base to the end of the operand
+};
+
 template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, bool VARLEN, int STAGES>
 struct GemmKernel {
   using Op = Mfma<OP, FA, FB>;
@@ -291,28 +320,170 @@ struct GemmKernel {
   static constexpr int kStageBytes = kABytes + kBBytes;
   static constexpr int kLdsBytes = kStageBytes * STAGES;
   static constexpr int kLoadsPerKTile = LA::kInstr + LB::kInstr;
-  static constexpr int kStripPitch = kWN + 4;  // floats per staged row (pad: no bank conflicts)
-  static_assert(4 * 32 * kStripPitch * 4 <= kLdsBytes, "epilogue strips must fit in the ring");
+  static constexpr int kMfmaPerStep = kMI * kNI;
+  static constexpr int kDsPerStep = kMI * reads_per_frag<A_K, kES>() + kNI * reads_per_frag<B_K, kES>();
+  // Epilogue: 16-row fp32 strips, one per wave, XOR-swizzled by row in 16-byte chunks.
+  static constexpr int kStripRows = 16;
+  static constexpr int kStripChunks = kWN / 4;
+  static_assert(STAGES >= 3, "the mainloop issues k-tile kt+STAGES-1 while reading kt+1");
+  static_assert(4 * kStripRows * kWN * 4 <= kStageBytes, "epilogue strips must fit in one stage");
 
-  // Scale, add beta*C, activate, convert and store one 32 x kWN strip staged in LDS.
+  // ---- scheduling hints: interleave LDS reads (and VMEM loads) with the MFMAs ----
+  // Group I: one MFMA, then one VMEM load (while any remain), then the next share of LDS
+  // reads; the builtin needs literal arguments, hence the compile-time recursion.
+  template <int NVMEM, int I = 0>
+  static __device__ __forceinline__ void sched_step() {
+    constexpr int M = kMfmaPerStep, D = kDsPerStep;
+    constexpr int per = (D + M - 1) / M;
+    if constexpr (I < M) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if constexpr (I < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one VMEM read
+      if constexpr (I * per < D) {
+        constexpr int n = (D - I * per) < per ? (D - I * per) : per;
+        __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // LDS reads
+      }
+      sched_step<NVMEM, I + 1>();
+    }
+  }
+
+  static __device__ __forceinline__ void read_step(Frag (&fa)[kMI], Frag (&fb)[kNI], const GEP_LDS char* st,
+                                                   int s, int wm0, int wn0, int lane) {
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) fa[i] = read_frag<A_K, BM, Op>(st, wm0 + i * 32, s, lane);
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) fb[j] = read_frag<B_K, BN, Op>(st + kABytes, wn0 + j * 32, s, lane);
+  }
+
+  static __device__ __forceinline__ void mma_step(f32x16 (&acc)[kMI][kNI], const Frag (&fa)[kMI],
+                                                  const Frag (&fb)[kNI]) {
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int j = 0; j < kNI; ++j) acc[i][j] = Op::mma(fb[j], fa[i], acc[i][j]);
+  }
+
+  // Wait until k-tile j has landed in LDS for every wave. It is called in iteration j - 1
+  // before that iteration issues k-tile j + STAGES - 2, so the k-tiles issued after j are
+  // j + 1 .. min(j + STAGES - 3, nk - 1): only their loads may stay outstanding.
+  static __device__ __forceinline__ void wait_ktile(int j, int nk) {
+    const int after = min(STAGES - 3, nk - 1 - j);
+    if constexpr (STAGES >= 5) {
+      if (after >= 2) { wait_vm_barrier<2 * kLoadsPerKTile>(); return; }
+    }
+    if (after >= 1) wait_vm_barrier<kLoadsPerKTile>();
+    else wait_vm_barrier<0>();
+  }
+
+  static __device__ __forceinline__ TileInfo decode(const KParams& p, int t, const int32_t* gstart) {
+    TileInfo ti;
+    uint32_t mb, nb;
+    int row_base;
+    if constexpr (VARLEN) {
+      int lo = 0, hi = p.L - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (gstart[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      ti.l = lo;
+      row_base = p.cu_seqlens[lo];
+      ti.row_end = p.cu_seqlens[lo + 1];
+      const uint32_t tmg = (uint32_t)((ti.row_end - row_base + BM - 1) / BM);
+      raster(p, (uint32_t)(t - gstart[lo]), tmg, mb, nb);
+    } else {
+      uint32_t ll, r;
+      fd_divmod(p.fd_mn, (uint32_t)t, ll, r);
+      raster(p, r, (uint32_t)p.tm, mb, nb);
+      ti.l = (int)ll;
+      row_base = 0;
+      ti.row_end = p.M;
+    }
+    ti.mb = (int)mb;
+    ti.nb = (int)nb;
+    ti.m0 = row_base + (int)mb * BM;
+    ti.n0 = (int)nb * BN;
+    const int64_t a_lb = VARLEN ? 0 : (int64_t)ti.l * p.sa;
+    const int64_t b_lb = (int64_t)ti.l * p.sb;
+    const int64_t a_off = (a_lb + (A_K ? (int64_t)ti.m0 * p.lda : (int64_t)ti.m0)) * kES;
+    const int64_t b_off = (b_lb + (B_K ? (int64_t)ti.n0 * p.ldb : (int64_t)ti.n0)) * kES;
+    ti.a_tile = (const char*)p.A + a_off;
+    ti.b_tile = (const char*)p.B + b_off;
+    ti.a_room = p.a_bytes - a_off;
+    ti.b_room = p.b_bytes - b_off;
+    return ti;
+  }
+
+  static __device__ __forceinline__ void issue(const KParams& p, const TileInfo& ti, const LA& la, const LB& lb,
+                                               GEP_LDS char* smem, int wave, int kt) {
+    GEP_LDS char* st = smem + (kt % STAGES) * kStageBytes;
+    const int64_t a_step = A_K ? (int64_t)kRowBytes : (int64_t)kBK * p.lda * kES;
+    const int64_t b_step = B_K ? (int64_t)kRowBytes : (int64_t)kBK * p.ldb * kES;
+    const int64_t ao = (int64_t)kt * a_step, bo = (int64_t)kt * b_step;
+    const bool tail = (kt + 1) * kBK > p.K;
+    la.issue(make_rsrc(ti.a_tile + ao, ti.a_room - ao), st, wave, kt * kBK, p.K, tail);
+    lb.issue(make_rsrc(ti.b_tile + bo, ti.b_room - bo), st + kABytes, wave, kt * kBK, p.K, tail);
+  }
+
+  static __device__ __forceinline__ void prologue(const KParams& p, const TileInfo& ti, LA& la, LB& lb,
+                                                  GEP_LDS char* smem, int wave, int lane, int nk) {
+    la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES);
+    lb.init(wave, lane, p.N - ti.n0, p.ldb * kES);
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(p, ti, la, lb, smem, wave, s);
+  }
+
+  // MFMAs on fragment buffer CUR while the next fragments are read into the other buffer.
+  template <int CUR, int NVMEM>
+  static __device__ __forceinline__ void step_with_reads(f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
+                                                         Frag (&fb)[2][kNI], const GEP_LDS char* st, int s,
+                                                         int wm0, int wn0, int lane) {
+    read_step(fa[CUR ^ 1], fb[CUR ^ 1], st, s, wm0, wn0, lane);
+    mma_step(acc, fa[CUR], fb[CUR]);
+    sched_step<NVMEM>();
+  }
+
+  // One k-tile: kSteps MFMA steps on the fragments in buffer P0 (step 0), P0^1 (step 1), ...
+  // The last step also waits for k-tile kt+1, issues the loads of kt+STAGES-1 and reads the
+  // first fragments of kt+1 into the buffer after it.
+  template <int P0>
+  static __device__ __forceinline__ void ktile(const KParams& p, const TileInfo& ti, const LA& la, const LB& lb,
+                                               GEP_LDS char* smem, f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
+                                               Frag (&fb)[2][kNI], int kt, int nk, int wave, int lane, int wm0,
+                                               int wn0) {
+    const GEP_LDS char* st = smem + (kt % STAGES) * kStageBytes;
+    if constexpr (kSteps == 2) {
+      step_with_reads<P0, 0>(acc, fa, fb, st, 1, wm0, wn0, lane);
+    }
+    constexpr int LAST = (P0 + kSteps - 1) & 1;
+    if (kt + 1 < nk) {
+      wait_ktile(kt + 1, nk);
+      if (kt + STAGES - 1 < nk) issue(p, ti, la, lb, smem, wave, kt + STAGES - 1);
+    }
+    // After the last k-tile this reads a stage that holds no live data; the fragments are
+    // never used. Keeping one MFMA path avoids a merge of every accumulator (which made
+    // the register allocator spill).
+    const GEP_LDS char* st1 = smem + ((kt + 1) % STAGES) * kStageBytes;
+    step_with_reads<LAST, LA::kInstr + LB::kInstr>(acc, fa, fb, st1, 0, wm0, wn0, lane);
+  }
+
+  // Scale, add beta*C, activate, convert and store one kStripRows x kWN strip staged in LDS.
   static __device__ __forceinline__ void epilogue_strip(const KParams& p, const float GEP_LDS* strip, int lane,
                                                         int mrow0, int ncol0, int row_end, int l, float alpha,
                                                         float beta) {
-    constexpr int kLanesPerRow = kWN / 4;
-    constexpr int kRowsPerIt = 64 / kLanesPerRow;
-    const int rr = lane / kLanesPerRow, cc = (lane % kLanesPerRow) * 4;
-    const int n = ncol0 + cc;
+    constexpr int kRowsPerIt = 64 / kStripChunks;
+    const int rr = lane / kStripChunks, q = lane % kStripChunks;
+    const int n = ncol0 + q * 4;
     if (n >= p.N) return;
     const int64_t c_lb = VARLEN ? 0 : (int64_t)l * p.sc;
     const int64_t d_lb = VARLEN ? 0 : (int64_t)l * p.sd;
     const int64_t p_lb = VARLEN ? 0 : (int64_t)l * p.sp;
     const int cb = dt_bytes(p.c_dt), db = dt_bytes(p.d_dt), pb = dt_bytes(p.p_dt);
 #pragma unroll 1
-    for (int it = 0; it < 32 / kRowsPerIt; ++it) {
+    for (int it = 0; it < kStripRows / kRowsPerIt; ++it) {
       const int row = it * kRowsPerIt + rr;
       const int m = mrow0 + row;
       if (m >= row_end) break;
-      const f32x4 x = *(const f32x4 GEP_LDS*)(strip + row * kStripPitch + cc);
+      const f32x4 x = *(const f32x4 GEP_LDS*)(strip + row * kWN + ((q ^ (row & 7)) << 2));
       float v[4] = {x[0] * alpha, x[1] * alpha, x[2] * alpha, x[3] * alpha};
       if (p.c_dt != DT_NONE) {
         float c[4];
@@ -330,10 +501,42 @@ struct GemmKernel {
     }
   }
 
+  // Accumulator lane layout: for block (i, j) and register group g, lane l holds row
+  // wm0 + 32i + (l % 32) and columns wn0 + 32j + 8g + 4(l / 32) + [0, 4).
+  static __device__ __forceinline__ void epilogue(const KParams& p, const TileInfo& ti,
+                                                  const f32x16 (&acc)[kMI][kNI], float GEP_LDS* region, int wave,
+                                                  int lane, int wm0, int wn0, float alpha, float beta) {
+    float GEP_LDS* strip = region + wave * kStripRows * kWN;
+    const int r16 = lane & 15;
+    const bool mine_lo = ((lane >> 4) & 1) == 0;  // lane holds rows 0..15 of its 32-row block
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (mine_lo == (h == 0)) {
+#pragma unroll
+          for (int j = 0; j < kNI; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                               acc[i][j][4 * g + 3]};
+              const int q = j * 8 + 2 * g + (lane >> 5);
+              *(f32x4 GEP_LDS*)(strip + r16 * kWN + ((q ^ (r16 & 7)) << 2)) = v;
+            }
+        }
+        // LDS operations of one wave complete in order; keep the compiler from reordering
+        asm volatile("" ::: "memory");
+        epilogue_strip(p, strip, lane, ti.m0 + wm0 + i * 32 + h * 16, ti.n0 + wn0, ti.row_end, ti.l, alpha, beta);
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+
   static __device__ __forceinline__ void run(const KParams& p) {
     __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
     GEP_LDS char* smem = (GEP_LDS char*)smem_raw;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     const int wm0 = (wave >> 1) * kWM, wn0 = (wave & 1) * kWN;
 
     const int P = p.P;
@@ -382,124 +585,60 @@ struct GemmKernel {
       T = s_start[G];
     }
 
-    float alpha = p.alpha_ptr ? *p.alpha_ptr : p.alpha;
-    float beta = p.beta_ptr ? *p.beta_ptr : p.beta;
+    const float alpha = p.alpha_ptr ? *p.alpha_ptr : p.alpha;
+    const float beta = p.beta_ptr ? *p.beta_ptr : p.beta;
+    // k-tiles; with one MFMA step per k-tile (fp8) the loop runs k-tiles in pairs, so an odd
+    // count gets one padding k-tile past K: its loads read zeros and it adds nothing.
+    int nk = (p.K + kBK - 1) / kBK;
+    if constexpr (kSteps % 2 != 0) nk = (nk + 1) & ~1;
+    float GEP_LDS* epi_region = (float GEP_LDS*)(smem + (STAGES - 1) * kStageBytes);
 
     LA la;
     LB lb;
+    Frag fa[2][kMI], fb[2][kNI];
+    TileInfo ti;
+    if (bb < T) {
+      ti = decode(p, bb, gstart);
+      prologue(p, ti, la, lb, smem, wave, lane, nk);
+    }
     int iter = 0;
     for (int t = bb; t < T; t += P, ++iter) {
-      // ---- decode the tile
-      uint32_t mb, nb;
-      int l, row_base, row_end;
-      if constexpr (VARLEN) {
-        int lo = 0, hi = p.L - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (gstart[mid] <= t) lo = mid; else hi = mid - 1;
-        }
-        l = lo;
-        row_base = p.cu_seqlens[l];
-        row_end = p.cu_seqlens[l + 1];
-        const uint32_t tmg = (uint32_t)((row_end - row_base + BM - 1) / BM);
-        raster(p, (uint32_t)(t - gstart[l]), tmg, mb, nb);
-      } else {
-        uint32_t ll, r;
-        fd_divmod(p.fd_mn, (uint32_t)t, ll, r);
-        raster(p, r, (uint32_t)p.tm, mb, nb);
-        l = (int)ll;
-        row_base = 0;
-        row_end = p.M;
-      }
       if (p.tile_log && iter < p.tile_log_iters && tid == 0) {
         int32_t* e = p.tile_log + ((int64_t)bid * p.tile_log_iters + iter) * 4;
-        e[0] = (int32_t)mb; e[1] = (int32_t)nb; e[2] = l; e[3] = t;
+        e[0] = ti.mb; e[1] = ti.nb; e[2] = ti.l; e[3] = t;
       }
-      const int m0 = row_base + (int)mb * BM;  // first row of the tile
-      const int n0 = (int)nb * BN;
-
-      // ---- operand tile bases (bytes) and loaders
-      const int64_t a_lb = VARLEN ? 0 : (int64_t)l * p.sa;
-      const int64_t b_lb = (int64_t)l * p.sb;
-      const char* a_tile;
-      const char* b_tile;
-      int64_t a_room, b_room;  // bytes from the tile base to the operand's end
-      {
-        const int64_t a_off = (a_lb + (A_K ? (int64_t)m0 * p.lda : (int64_t)m0)) * kES;
-        const int64_t b_off = (b_lb + (B_K ? (int64_t)n0 * p.ldb : (int64_t)n0)) * kES;
-        a_tile = (const char*)p.A + a_off;
-        b_tile = (const char*)p.B + b_off;
-        a_room = p.a_bytes - a_off;
-        b_room = p.b_bytes - b_off;
-      }
-      const int64_t lda_b = p.lda * kES, ldb_b = p.ldb * kES;
-      la.init(wave, lane, row_end - m0, lda_b);
-      lb.init(wave, lane, p.N - n0, ldb_b);
-      const int64_t a_kstep = A_K ? (int64_t)kRowBytes : (int64_t)kBK * lda_b;
-      const int64_t b_kstep = B_K ? (int64_t)kRowBytes : (int64_t)kBK * ldb_b;
-
-      const int nk = (p.K + kBK - 1) / kBK;
-      auto issue = [&](int kt) {
-        GEP_LDS char* st = smem + (kt % STAGES) * kStageBytes;
-        const int64_t ao = (int64_t)kt * a_kstep, bo = (int64_t)kt * b_kstep;
-        la.issue(make_rsrc(a_tile + ao, a_room - ao), st, wave, kt * kBK, p.K);
-        lb.issue(make_rsrc(b_tile + bo, b_room - bo), st + kABytes, wave, kt * kBK, p.K);
-      };
-
       f32x16 acc[kMI][kNI];
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
 #pragma unroll
         for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
 
-      // every wave is done with the previous tile's LDS before it is overwritten
-      barrier_only();
-#pragma unroll
-      for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) issue(s);
-
-      for (int kt = 0; kt < nk; ++kt) {
-        if (kt + STAGES - 2 < nk) wait_vm_barrier<(STAGES - 2) * kLoadsPerKTile>();
-        else wait_vm_barrier<0>();
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-        const GEP_LDS char* sa = smem + (kt % STAGES) * kStageBytes;
-        const GEP_LDS char* sb = sa + kABytes;
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          Frag af[kMI], bf[kNI];
-#pragma unroll
-          for (int i = 0; i < kMI; ++i) af[i] = read_frag<A_K, BM, Op>(sa, wm0 + i * 32, s, lane);
-#pragma unroll
-          for (int j = 0; j < kNI; ++j) bf[j] = read_frag<B_K, BN, Op>(sb, wn0 + j * 32, s, lane);
-#pragma unroll
-          for (int i = 0; i < kMI; ++i)
-#pragma unroll
-            for (int j = 0; j < kNI; ++j) acc[i][j] = Op::mma(bf[j], af[i], acc[i][j]);
+      if (nk > 0) {
+        // The previous tile's epilogue issued loads and stores after this tile's prologue
+        // loads; loads and stores share vmcnt but need not complete in order with respect
+        // to each other, so only a full drain proves that k-tile 0 has landed.
+        wait_vm_barrier<0>();
+        read_step(fa[0], fb[0], smem, 0, wm0, wn0, lane);
+        if constexpr (kSteps % 2 == 0) {
+          for (int kt = 0; kt < nk; ++kt)
+            ktile<0>(p, ti, la, lb, smem, acc, fa, fb, kt, nk, wave, lane, wm0, wn0);
+        } else {
+          for (int kt = 0; kt < nk; kt += 2) {
+            ktile<0>(p, ti, la, lb, smem, acc, fa, fb, kt, nk, wave, lane, wm0, wn0);
+            ktile<1>(p, ti, la, lb, smem, acc, fa, fb, kt + 1, nk, wave, lane, wm0, wn0);
+          }
         }
       }
 
-      // ---- epilogue. Lane l holds, for block (i, j) and register group g, the values at
-      // row wm0 + 32i + (l % 32), columns wn0 + 32j + 8g + 4(l / 32) + [0, 4). Each
-      // 32-row strip goes through this wave's part of the (now idle) LDS ring as fp32 and
-      // comes back row-contiguous: 4 consecutive columns per lane, so C loads and D /
-      // PostAct stores are coalesced.
+      // ---- next tile's first k-tiles go in flight, then this tile's epilogue
       barrier_only();  // every wave is done reading the ring
-      float GEP_LDS* strip = (float GEP_LDS*)smem + wave * 32 * kStripPitch;
-#pragma unroll
-      for (int i = 0; i < kMI; ++i) {
-#pragma unroll
-        for (int j = 0; j < kNI; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                             acc[i][j][4 * g + 3]};
-            *(f32x4 GEP_LDS*)(strip + (lane & 31) * kStripPitch + j * 32 + 8 * g + 4 * (lane >> 5)) = v;
-          }
-        // LDS operations of one wave complete in order; keep the compiler from reordering
-        asm volatile("" ::: "memory");
-        epilogue_strip(p, strip, lane, m0 + wm0 + i * 32, n0 + wn0, row_end, l, alpha, beta);
-        asm volatile("" ::: "memory");
+      const TileInfo cur = ti;
+      const int tnext = t + P;
+      if (tnext < T) {
+        ti = decode(p, tnext, gstart);
+        prologue(p, ti, la, lb, smem, wave, lane, nk);
       }
+      epilogue(p, cur, acc, epi_region, wave, lane, wm0, wn0, alpha, beta);
     }
   }
 };
