@@ -6,10 +6,10 @@
 
 namespace gep {
 
-constexpr int kStages = 4;
+constexpr int kStages = 2;
 
-// Workgroups per CU the kernel is built for: 256x256 tiles hold 4 x 32 KB of LDS (one per CU),
-// 128x128 tiles 4 x 16 KB (two per CU).
+// Workgroups per CU the kernel is built for: 256x256 tiles keep 256 accumulators per lane
+// (one workgroup per CU); 128x128 tiles fit two per CU.
 template <int BM>
 constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
 
