@@ -105,16 +105,21 @@ def cpu_baseline(inp, budget_s=15.0):
                       f"{flops / 1e9:.1f} GFLOP) in {dt:.1f} s, fp64 k-ascending dot products"}
 
 
-def traffic_for(name, launches_ms):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+def traffic_for(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/gemm_persistent_kernel_<workload>_traffic.md), if it was taken on the current
+    kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"gemm_persistent_kernel_{name}_traffic.md")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    rec = {}
+    for line in open(path):
+        if " = " in line:
+            k, v = line.split(" = ", 1)
+            rec[k.strip()] = v.strip()
     if rec.get("source_hash") != source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def main():
@@ -155,7 +160,7 @@ def main():
     flops = inp.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[inp.a_dt]
-    traffic = traffic_for(a.workload, ms)
+    traffic = traffic_for(a.workload)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4), "traffic": traffic,
             "kernel": "gemm_persistent_kernel", "algorithmic_bytes": algorithmic_bytes(inp),
