@@ -8,27 +8,33 @@
 //   * 256 threads = 4 wave64s in a 2x2 grid; each wave owns a (BM/2) x (BN/2) block of the
 //     output tile, computed with v_mfma_f32_32x32x16_{f16,bf16} or, for fp8,
 //     v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales; per-operand e4m3/e5m2 format fields).
-//   * A and B k-tiles of 64 bytes per row travel global -> LDS with buffer_load ... lds
-//     (no VGPR staging) into a STAGES-deep ring, issued STAGES-1 k-tiles ahead.
-//     Out-of-range rows / k-chunks use an offset past the buffer's num_records, which the
-//     hardware reads as zero (tails in M, N and K).
-//   * K-major tiles are stored [row][4 x 16-byte chunks] with the chunk index XOR-swizzled
+//   * A k-tile is 128 bytes of K per row (64 16-bit or 128 fp8 elements): every global load
+//     instruction reads whole 128-byte lines. A and B k-tiles travel global -> VGPRs
+//     (buffer_load_dwordx4, one staging register set) -> LDS (ds_write_b128) into a
+//     two-stage ring. Out-of-range rows / k-chunks use an offset past the buffer's
+//     num_records, which the hardware reads as zero (tails in M, N and K).
+//   * Each k-tile: the register set (k-tile kt+1) is written to the free stage during the
+//     first MFMA steps, every chunk reloaded from k-tile kt+2 right after its write; one
+//     barrier per k-tile, before the last MFMA step, whose fragment reads already come from
+//     the next stage.
+//   * K-major tiles are stored [row][8 x 16-byte chunks] with the chunk index XOR-swizzled
 //     by the row, so the 32-row MFMA fragment reads (ds_read_b128) hit distinct banks.
 //     M/N-major (16-bit) tiles are stored [k][row] and read with ds_read_b64_tr_b16, which
 //     transposes 16x4 blocks across each 16-lane group into K-contiguous fragments.
 //   * Fragments are double-buffered in registers: the LDS reads of the next k-step are
-//     interleaved with the MFMAs of the current one. The once-per-k-tile barrier sits before
-//     the last k-step's MFMAs, so the next k-tile's first fragments load under them.
+//     interleaved with the MFMAs of the current one.
 //   * Persistent grid: workgroup b takes tiles t = b' + i*P; t -> (m_blk, n_blk, l) by the
 //     grouped raster with FastDivmod (page 6, quack/fast_math.py); b' optionally remaps b so
 //     that the workgroups of one XCD (dispatched round-robin) take consecutive tile ids.
-//   * Epilogue: the accumulators go, 16 rows at a time, through one stage-sized region of
-//     the ring as fp32 and come back row-contiguous (4 columns per lane) for scaling,
+//   * Epilogue: the accumulators go, 16 rows at a time, through per-wave fp32 strips in the
+//     (then idle) ring and come back row-contiguous (4 columns per lane) for scaling,
 //     beta*C, the activation, conversion and coalesced stores. The next tile's first k-tile
-//     loads are already in flight in the other stages meanwhile.
+//     loads are already in flight into the staging registers meanwhile.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "params.hpp"
 
@@ -91,16 +97,16 @@ struct Mfma<OP_FP8, FA, FB> {
 // ------------------------------------------------------------------------------------
 // LDS tile layouts
 // ------------------------------------------------------------------------------------
-constexpr int kRowBytes = 64;  // bytes of K per row of a K-major k-tile
+constexpr int kRowBytes = 128;  // bytes of K per row of a K-major k-tile
 constexpr int kChunks = kRowBytes / 16;
 
 // K-major: 16-byte chunk c of row r lives at chunk c ^ kswz(r). Measured on gfx950, a
 // ds_read_b128 is served in 4 phases of 16 lanes (the lanes sharing lane bit 5 and
 // bit 2 ^ bit 4) over 64 four-byte banks, i.e. one 256-byte window per phase. A fragment
-// read puts rows r0 + (l % 32) of one logical chunk in a phase; 64-byte rows sharing r & 3
-// land in the same 64-byte quarter of the window, so the key must differ between them:
-// (r >> 2) & 3 does, for both phase parities.
-__device__ __forceinline__ int kswz(int row) { return (row >> 2) & 3; }
+// read puts rows r0 + (l % 32) of one logical chunk in a phase: per value of row bit 0
+// (which 128-byte half of the window a row falls in), eight rows that differ in bits 1..3.
+// Keyed by those bits, the chunk lands in eight distinct 16-byte slots of its half.
+__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
 // M/N-major: chunk c of k-row k lives at chunk c ^ mswz(k); the 4 k-rows that one 16-lane
 // transpose group reads land in 4 disjoint 64-byte bank ranges.
 __device__ __forceinline__ int mswz(int k) { return (k & 3) << 2; }
@@ -115,8 +121,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // VGPRs: each lane loads kInstr 16-byte chunks (buffer_load_dwordx4) and later writes them
 // with ds_write_b128 to fixed LDS positions (block q*4+wave of 1 KB, lane*16 inside it).
 // The global address of a lane is the inverse of the LDS swizzle, so LDS writes are
-// contiguous and conflict-free. Measured on gfx950, this path keeps the MFMA pipe full at
-// twice the bandwidth the mainloop needs, where LDS-DMA loads (buffer_load ... lds) slow it.
+// contiguous and conflict-free, and the 8 (K-major) or 32/16 (M/N-major) lanes that fill
+// one LDS row read one contiguous 128/512/256-byte run of global memory.
 template <int ROWS, bool KMAJ, int ES>
 struct TileLoader {
   static constexpr int kTileBytes = ROWS * kRowBytes;
@@ -126,8 +132,12 @@ struct TileLoader {
   static_assert(kInstr >= 1, "tile too small for 4 waves");
   uint32_t offv[kInstr];   // byte offset of this lane's chunk in the k-tile, or kOOB when the
                            // row / column chunk lies outside the operand
-  int32_t klim[kInstr];    // the chunk exists while k0 < klim (K minus its k offset in the k-tile)
-  i32x4 reg[2][kInstr];    // two staging sets (k-tile parity)
+  int32_t klim;            // chunk q exists while k0 + q * kDK < klim (K minus the chunk's
+                           // k offset in the k-tile)
+  i32x4 reg[kInstr];       // staging registers
+  // k offset between consecutive chunks of a lane: K-major chunks of one lane share their
+  // k offset (the swizzle key repeats every 32 rows); M/N-major ones step 4*kKPI k-rows
+  static constexpr int kDK = KMAJ ? 0 : 4 * kKPI;
 
   // rows_valid: rows of this tile that exist (K-major) or MN elements that exist (MN-major).
   __device__ __forceinline__ void init(int wave, int lane, int rows_valid, int64_t ld_bytes, int K) {
@@ -138,30 +148,30 @@ struct TileLoader {
         const int row = blk * (1024 / kRowBytes) + lane / kChunks;
         const int c = (lane % kChunks) ^ kswz(row);
         offv[q] = row < rows_valid ? (uint32_t)(row * ld_bytes + c * 16) : kOOB;
-        klim[q] = K - c * (16 / ES);
       } else {
         const int krow = blk * kKPI + lane / kCPR;
         const int c = (lane % kCPR) ^ mswz(krow);
         offv[q] = c * (16 / ES) < rows_valid ? (uint32_t)(krow * ld_bytes + c * 16) : kOOB;
-        klim[q] = K - krow;
       }
+    }
+    if constexpr (KMAJ) {
+      klim = K - (((lane % kChunks) ^ kswz(wave * (1024 / kRowBytes) + lane / kChunks)) * (16 / ES));
+    } else {
+      klim = K - (wave * kKPI + lane / kCPR);
     }
   }
 
-  // Global -> registers. Chunks at k >= K (the K tail, and whole k-tiles past the end) read
-  // as zero through the buffer range check.
-  template <int SET>
+  // Global -> registers, chunk Q of the k-tile starting at element k0 of K. Chunks at
+  // k >= K (the K tail, and whole k-tiles past the end) read as zero.
+  template <int Q>
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int k0) {
-#pragma unroll
-    for (int q = 0; q < kInstr; ++q)
-      reg[SET][q] = __builtin_amdgcn_raw_buffer_load_b128(rs, k0 < klim[q] ? offv[q] : kOOB, 0, 0);
+    reg[Q] = __builtin_amdgcn_raw_buffer_load_b128(rs, k0 + Q * kDK < klim ? offv[Q] : kOOB, 0, 0);
   }
 
-  // Registers -> LDS (tile base `lds`).
-  template <int SET>
+  // Registers -> LDS (tile base `lds`), chunk Q.
+  template <int Q>
   __device__ __forceinline__ void store(GEP_LDS char* lds, int wave, int lane) const {
-#pragma unroll
-    for (int q = 0; q < kInstr; ++q) *(GEP_LDS i32x4*)(lds + (q * 4 + wave) * 1024 + lane * 16) = reg[SET][q];
+    *(GEP_LDS i32x4*)(lds + (Q * 4 + wave) * 1024 + lane * 16) = reg[Q];
   }
 };
 
@@ -181,7 +191,7 @@ __device__ __forceinline__ typename Op::Frag read_frag(const GEP_LDS char* tile,
       const int c = s * 2 + (lane >> 5);
       return *(const GEP_LDS i32x4*)(rp + ((c ^ sw) << 4));
     } else {
-      const int c = (lane >> 5) * 2;  // one fp8 k-step spans the whole 64-byte row
+      const int c = s * 4 + (lane >> 5) * 2;  // 32 bytes per lane: two chunks
       i32x4 lo = *(const GEP_LDS i32x4*)(rp + ((c ^ sw) << 4));
       i32x4 hi = *(const GEP_LDS i32x4*)(rp + (((c + 1) ^ sw) << 4));
       return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -217,53 +227,51 @@ __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp
 
 // Activation of the fp32 pre-activation value (page 6, gemm_act_sm90.py, act_fn_map; SiLU
 // added here). Both smooth activations are x * sigmoid(z): GELU-tanh uses
-// 0.5 * (1 + tanh(u)) = sigmoid(2u) with u = sqrt(2/pi) * (x + 0.044715 x^3).
-__device__ __forceinline__ float apply_act(int act, float x) {
-  switch (act) {
-    case ACT_RELU: return x > 0.f ? x : 0.f;
-    case ACT_RELU_SQ: { float r = x > 0.f ? x : 0.f; return r * r; }
-    case ACT_GELU_TANH: {
-      const float u2 = 1.5957691216057308f * (x + 0.044715f * x * x * x);  // 2u
-      return x / (1.f + fast_exp(-u2));
-    }
-    case ACT_SILU: return x / (1.f + fast_exp(-x));
-    default: return x;
+// 0.5 * (1 + tanh(u)) = sigmoid(2u) with u = sqrt(2/pi) * (x + 0.044715 x^3). The
+// reciprocal is v_rcp_f32 (1 ulp), far below the bf16/f16 rounding of the result.
+template <int ACT>
+__device__ __forceinline__ float act_fn(float x) {
+  if constexpr (ACT == ACT_RELU) {
+    return x > 0.f ? x : 0.f;
+  } else if constexpr (ACT == ACT_RELU_SQ) {
+    const float r = x > 0.f ? x : 0.f;
+    return r * r;
+  } else if constexpr (ACT == ACT_GELU_TANH) {
+    const float u2 = 1.5957691216057308f * (x + 0.044715f * x * x * x);  // 2u
+    return x * __builtin_amdgcn_rcpf(1.f + fast_exp(-u2));
+  } else if constexpr (ACT == ACT_SILU) {
+    return x * __builtin_amdgcn_rcpf(1.f + fast_exp(-x));
+  } else {
+    return x;
   }
 }
 
-__device__ __forceinline__ void load4(const void* p, int dt, float v[4]) {
-  if (dt == DT_F32) {
-    float4 x = *(const float4*)p;
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-  } else if (dt == DT_BF16) {
-    uint2 x = *(const uint2*)p;
+// Four fp32 values as the 8 bytes of 4 bf16 / f16 (round to nearest even).
+__device__ __forceinline__ uint2 pack4_16(int dt, const float v[4]) {
+  uint2 x;
+  if (dt == DT_BF16) {
+    __bf16 h[4] = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    __builtin_memcpy(&x, h, 8);
+  } else {
+    _Float16 h[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    __builtin_memcpy(&x, h, 8);
+  }
+  return x;
+}
+
+// Four consecutive 16-bit values (bf16 or f16) to fp32.
+__device__ __forceinline__ void unpack4_16(int dt, uint2 x, float v[4]) {
+  if (dt == DT_BF16) {
     v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
     v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
   } else {
-    uint2 x = *(const uint2*)p;
     _Float16 h[4];
     __builtin_memcpy(h, &x, 8);
     v[0] = (float)h[0]; v[1] = (float)h[1]; v[2] = (float)h[2]; v[3] = (float)h[3];
   }
 }
 
-__device__ __forceinline__ void store4(void* p, int dt, const float v[4]) {
-  if (dt == DT_F32) {
-    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
-  } else if (dt == DT_BF16) {
-    __bf16 h[4] = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-    uint2 x;
-    __builtin_memcpy(&x, h, 8);
-    *(uint2*)p = x;
-  } else {
-    _Float16 h[4] = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-    uint2 x;
-    __builtin_memcpy(&x, h, 8);
-    *(uint2*)p = x;
-  }
-}
-
-__device__ __forceinline__ int dt_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
+__device__ __forceinline__ int dt_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_NONE ? 0 : 2); }
 
 // Complete this wave's LDS operations, then synchronise the workgroup. The "memory"
 // clobber keeps LDS accesses on their side of it.
@@ -311,66 +319,52 @@ struct TileInfo {
   int64_t a_room, b_room;  // bytes from the tile base to the end of the operand
 };
 
-template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, bool VARLEN, int STAGES>
+
+template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, bool VARLEN>
 struct GemmKernel {
   using Op = Mfma<OP, FA, FB>;
   using Frag = typename Op::Frag;
   static constexpr int kES = Op::kES;
   static constexpr int kBK = kRowBytes / kES;             // K elements per k-tile
-  static constexpr int kSteps = kBK / Op::kKStep;          // MFMA k-steps per k-tile
+  static constexpr int kSteps = kBK / Op::kKStep;          // MFMA k-steps per k-tile (4 or 2)
   static constexpr int kWM = BM / 2, kWN = BN / 2;         // per-wave output block
   static constexpr int kMI = kWM / 32, kNI = kWN / 32;     // 32x32 MFMA blocks per wave
   using LA = TileLoader<BM, A_K, kES>;
   using LB = TileLoader<BN, B_K, kES>;
   static constexpr int kABytes = LA::kTileBytes, kBBytes = LB::kTileBytes;
   static constexpr int kStageBytes = kABytes + kBBytes;
-  static constexpr int kEpiBytes = 4 * 16 * (BN / 2) * 4;      // 16-row fp32 strip per wave
-  static constexpr int kLdsBytes = kStageBytes * STAGES + kEpiBytes;
-  static constexpr int kLoadsPerKTile = LA::kInstr + LB::kInstr;
+  static constexpr int kLdsBytes = 2 * kStageBytes;
+  static constexpr int kFrags = kMI + kNI;
   static constexpr int kMfmaPerStep = kMI * kNI;
-  static constexpr int kDsPerStep = kMI * reads_per_frag<A_K, kES>() + kNI * reads_per_frag<B_K, kES>();
-  // Epilogue: 16-row fp32 strips, one per wave, XOR-swizzled by row in 16-byte chunks.
-  static constexpr int kStripRows = 16;
-  static constexpr int kStripChunks = kWN / 4;
-  static_assert(STAGES == 2, "the mainloop alternates two LDS stages");
-  // k-tile kt+kW is written to LDS in k-tile kt, and loaded into registers kLead k-tiles
-  // before that (two register sets)
-  static constexpr int kW = kSteps == 2 ? 1 : 2;
+  static constexpr int kRA = reads_per_frag<A_K, kES>(), kRB = reads_per_frag<B_K, kES>();
+  // register chunks of one k-tile, written to LDS (and reloaded) over the first kWriteSteps
+  // MFMA steps, kCPF chunks next to each fragment read
+  static constexpr int kChunksPerKt = LA::kInstr + LB::kInstr;
+  static constexpr int kWriteSteps = kSteps >= 4 ? 2 : 1;
+  static constexpr int kChunksPerStep = kChunksPerKt / kWriteSteps;
+  static constexpr int kCPF = kChunksPerStep / kFrags;
+  static constexpr int kMPF = kMfmaPerStep / kFrags;       // MFMAs per fragment slot
+  static_assert(kSteps % 2 == 0, "a k-tile ends on fragment buffer 0");
+  static_assert(kChunksPerKt % kWriteSteps == 0 && kChunksPerStep % kFrags == 0 && kCPF >= 1,
+                "register chunks must spread evenly over the fragment slots");
+  static_assert(kMfmaPerStep % kFrags == 0 && kMPF >= 1, "MFMAs must spread evenly over the fragment slots");
 
-  // ---- scheduling hints: interleave LDS reads (and VMEM loads) with the MFMAs ----
-  // Scheduling pattern of one MFMA step, in groups that each start with one MFMA. Without
-  // staging (NST == 0) the step's LDS reads are spread over all its MFMAs. With staging the
-  // first half of the MFMAs carries the LDS reads and the second half the LDS writes and
-  // the VMEM loads: the reads must stay ahead of the writes (the compiler cannot prove
-  // them disjoint), and they are what the next step waits for. The builtin needs literal
+  // ---- scheduling hints: one slot per fragment, each carrying kMPF MFMAs, the fragment's
+  // LDS reads and (WR) kCPF LDS writes and global loads, in that order. Program order
+  // already interleaves the memory operations the same way (the compiler keeps LDS reads
+  // and writes it cannot prove disjoint in program order). The builtin needs literal
   // arguments, hence the compile-time recursion.
-  template <int NST, int I = 0>
+  template <bool WR, int F = 0>
   static __device__ __forceinline__ void sched_step() {
-    constexpr int M = kMfmaPerStep, D = kDsPerStep;
-    constexpr int H = NST ? (M / 2 > 0 ? M / 2 : 1) : M;   // MFMAs that carry the reads
-    constexpr int rper = (D + H - 1) / H;
-    constexpr int wper = NST ? (NST + (M - H) - 1) / (M - H > 0 ? M - H : 1) : 0;
-    if constexpr (I < M) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if constexpr (I < H && I * rper < D) {
-        constexpr int n = (D - I * rper) < rper ? (D - I * rper) : rper;
-        __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // LDS reads
+    if constexpr (F < kFrags) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kMPF, 0);                     // MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, F < kMI ? kRA : kRB, 0);      // LDS reads
+      if constexpr (WR) {
+        __builtin_amdgcn_sched_group_barrier(0x200, kCPF, 0);                   // LDS writes
+        __builtin_amdgcn_sched_group_barrier(0x020, kCPF, 0);                   // VMEM loads
       }
-      if constexpr (I >= H && (I - H) * wper < NST) {
-        constexpr int n = (NST - (I - H) * wper) < wper ? (NST - (I - H) * wper) : wper;
-        __builtin_amdgcn_sched_group_barrier(0x200, n, 0);  // LDS writes
-        __builtin_amdgcn_sched_group_barrier(0x020, n, 0);  // VMEM loads
-      }
-      sched_step<NST, I + 1>();
+      sched_step<WR, F + 1>();
     }
-  }
-
-  static __device__ __forceinline__ void read_step(Frag (&fa)[kMI], Frag (&fb)[kNI], const GEP_LDS char* st,
-                                                   int s, int wm0, int wn0, int lane) {
-#pragma unroll
-    for (int i = 0; i < kMI; ++i) fa[i] = read_frag<A_K, BM, Op>(st, wm0 + i * 32, s, lane);
-#pragma unroll
-    for (int j = 0; j < kNI; ++j) fb[j] = read_frag<B_K, BN, Op>(st + kABytes, wn0 + j * 32, s, lane);
   }
 
   static __device__ __forceinline__ void mma_step(f32x16 (&acc)[kMI][kNI], const Frag (&fa)[kMI],
@@ -379,6 +373,14 @@ struct GemmKernel {
     for (int i = 0; i < kMI; ++i)
 #pragma unroll
       for (int j = 0; j < kNI; ++j) acc[i][j] = Op::mma(fb[j], fa[i], acc[i][j]);
+  }
+
+  static __device__ __forceinline__ void read_all(Frag (&fa)[kMI], Frag (&fb)[kNI], const GEP_LDS char* st, int s,
+                                                  int wm0, int wn0, int lane) {
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) fa[i] = read_frag<A_K, BM, Op>(st, wm0 + i * 32, s, lane);
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) fb[j] = read_frag<B_K, BN, Op>(st + kABytes, wn0 + j * 32, s, lane);
   }
 
   static __device__ __forceinline__ TileInfo decode(const KParams& p, int t, const int32_t* gstart) {
@@ -419,153 +421,208 @@ struct GemmKernel {
     return ti;
   }
 
-  // Global loads of k-tile j into register set SET (k-tiles past the end read as zero).
-  template <int SET>
-  static __device__ __forceinline__ void load_kt(const KParams& p, const TileInfo& ti, LA& la, LB& lb, int j) {
+  // Buffer resources of k-tile j of the current tile (k-tiles past the end read as zero).
+  struct KtSrc {
+    __amdgpu_buffer_rsrc_t a, b;
+    int k0;
+  };
+  static __device__ __forceinline__ KtSrc kt_src(const KParams& p, const TileInfo& ti, int j) {
     const int64_t a_step = A_K ? (int64_t)kRowBytes : (int64_t)kBK * p.lda * kES;
     const int64_t b_step = B_K ? (int64_t)kRowBytes : (int64_t)kBK * p.ldb * kES;
     const int64_t ao = (int64_t)j * a_step, bo = (int64_t)j * b_step;
-    la.template load<SET>(make_rsrc(ti.a_tile + ao, ti.a_room - ao), j * kBK);
-    lb.template load<SET>(make_rsrc(ti.b_tile + bo, ti.b_room - bo), j * kBK);
-  }
-  // Register set SET -> LDS stage of k-tile j.
-  template <int SET>
-  static __device__ __forceinline__ void store_kt(const LA& la, const LB& lb, GEP_LDS char* smem, int j, int wave,
-                                                  int lane) {
-    GEP_LDS char* st = smem + (j % STAGES) * kStageBytes;
-    la.template store<SET>(st, wave, lane);
-    lb.template store<SET>(st + kABytes, wave, lane);
+    return KtSrc{make_rsrc(ti.a_tile + ao, ti.a_room - ao), make_rsrc(ti.b_tile + bo, ti.b_room - bo), j * kBK};
   }
 
-  // First loads of a tile into registers: k-tile 0 (set 0) and 1 (set 1).
-  static __device__ __forceinline__ void prologue_loads(const KParams& p, const TileInfo& ti, LA& la, LB& lb,
-                                                        int wave, int lane) {
-    la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES, p.K);
-    lb.init(wave, lane, p.N - ti.n0, p.ldb * kES, p.K);
-    load_kt<0>(p, ti, la, lb, 0);
-    load_kt<1>(p, ti, la, lb, 1);
+  // Register chunk C (A chunks first, then B): write it to the LDS stage `wr`, then reload it
+  // from the k-tile described by `src`.
+  template <int C>
+  static __device__ __forceinline__ void cycle_chunk(LA& la, LB& lb, GEP_LDS char* wr, const KtSrc& src, int wave,
+                                                     int lane) {
+    if constexpr (C < LA::kInstr) {
+      la.template store<C>(wr, wave, lane);
+      la.template load<C>(src.a, src.k0);
+    } else {
+      lb.template store<C - LA::kInstr>(wr + kABytes, wave, lane);
+      lb.template load<C - LA::kInstr>(src.b, src.k0);
+    }
   }
-  // Rest of a tile's start (every wave is done reading the ring): k-tiles 0 .. kW-1 to LDS,
-  // their register sets reloaded with k-tiles 2 .. kW+1.
-  static __device__ __forceinline__ void prologue_stores(const KParams& p, const TileInfo& ti, LA& la, LB& lb,
-                                                         GEP_LDS char* smem, int wave, int lane) {
-    store_kt<0>(la, lb, smem, 0, wave, lane);
-    load_kt<0>(p, ti, la, lb, 2);
-    if constexpr (kW == 2) {
-      store_kt<1>(la, lb, smem, 1, wave, lane);
-      load_kt<1>(p, ti, la, lb, 3);
+  template <int C0, int N>
+  static __device__ __forceinline__ void cycle_chunks(LA& la, LB& lb, GEP_LDS char* wr, const KtSrc& src, int wave,
+                                                      int lane) {
+    if constexpr (N > 0) {
+      cycle_chunk<C0>(la, lb, wr, src, wave, lane);
+      cycle_chunks<C0 + 1, N - 1>(la, lb, wr, src, wave, lane);
+    }
+  }
+  // Only the loads (the tile's first k-tile).
+  template <int C = 0>
+  static __device__ __forceinline__ void load_all(LA& la, LB& lb, const KtSrc& src) {
+    if constexpr (C < kChunksPerKt) {
+      if constexpr (C < LA::kInstr) la.template load<C>(src.a, src.k0);
+      else lb.template load<C - LA::kInstr>(src.b, src.k0);
+      load_all<C + 1>(la, lb, src);
     }
   }
 
-  // MFMAs on fragment buffer CUR while the next fragments are read into the other buffer,
-  // and (STAGE) the register set of k-tile js is written to LDS and reloaded with k-tile jl.
-  // Program order puts the reads first: the compiler keeps LDS reads behind LDS writes it
-  // cannot prove disjoint, and the reads are the ones the next step waits for.
-  template <int CUR, bool STAGE, int SET>
-  static __device__ __forceinline__ void step(const KParams& p, const TileInfo& ti, LA& la, LB& lb,
-                                              GEP_LDS char* smem, f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
-                                              Frag (&fb)[2][kNI], const GEP_LDS char* st, int s, int js, int jl,
-                                              int wave, int lane, int wm0, int wn0) {
-    read_step(fa[CUR ^ 1], fb[CUR ^ 1], st, s, wm0, wn0, lane);
-    if constexpr (STAGE) {
-      store_kt<SET>(la, lb, smem, js, wave, lane);
-      load_kt<SET>(p, ti, la, lb, jl);
+  // Fragment slot F of a step: read fragment F (A fragments first) of k-step s into `fa`/
+  // `fb`, then (WR) cycle kCPF register chunks starting at C0 + F * kCPF.
+  template <bool WR, int C0, int F = 0>
+  static __device__ __forceinline__ void slots(Frag (&fa)[kMI], Frag (&fb)[kNI], const GEP_LDS char* rd, int s,
+                                               int wm0, int wn0, LA& la, LB& lb, GEP_LDS char* wr,
+                                               const KtSrc& src, int wave, int lane) {
+    if constexpr (F < kFrags) {
+      if constexpr (F < kMI) fa[F] = read_frag<A_K, BM, Op>(rd, wm0 + F * 32, s, lane);
+      else fb[F - kMI] = read_frag<B_K, BN, Op>(rd + kABytes, wn0 + (F - kMI) * 32, s, lane);
+      if constexpr (WR) cycle_chunks<C0 + F * kCPF, kCPF>(la, lb, wr, src, wave, lane);
+      slots<WR, C0, F + 1>(fa, fb, rd, s, wm0, wn0, la, lb, wr, src, wave, lane);
     }
+  }
+
+  // One MFMA step: MFMAs on fragment buffer CUR while the fragments of k-step s of the stage
+  // at `rd` are read into the other buffer; WR: register chunks [C0, C0 + kChunksPerStep)
+  // are written to the stage at `wr` and reloaded from `src`.
+  template <int CUR, bool WR, int C0>
+  static __device__ __forceinline__ void step(f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI], Frag (&fb)[2][kNI],
+                                              const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
+                                              const KtSrc& src, int wave, int lane, int wm0, int wn0) {
+    slots<WR, C0>(fa[CUR ^ 1], fb[CUR ^ 1], rd, s, wm0, wn0, la, lb, wr, src, wave, lane);
     mma_step(acc, fa[CUR], fb[CUR]);
-    sched_step<STAGE ? LA::kInstr + LB::kInstr : 0>();
+    sched_step<WR>();
   }
 
-  // One k-tile kt (PAR = kt & 1), the same code for every kt. k-tiles past the end are
-  // zero-filled and never used, so there is no branch and the LDS writes, loads and reads
-  // interleave with the MFMAs.
-  //   two MFMA steps (16-bit): step 0 writes k-tile kt+1 to LDS from its register set and
-  //     reloads that set with kt+3, while its MFMAs run on fragments of (kt, 0) and it reads
-  //     (kt, 1); barrier; step 1 runs (kt, 1) and reads (kt+1, 0).
-  //   one MFMA step (fp8): barrier; write kt+2, reload its set with kt+4, MFMAs on kt, read
-  //     kt+1.
-  // The barrier is preceded by lgkmcnt(0): this wave's LDS writes are complete and its
-  // reads of the stage about to be overwritten have returned.
+  // Steps S .. kSteps-2 of a k-tile (stage `cur`): step S runs the MFMAs of k-step S on
+  // buffer S & 1 and reads k-step S+1; the first kWriteSteps steps also cycle their share of
+  // the register chunks through the stage `nxt`.
+  template <int S = 0>
+  static __device__ __forceinline__ void first_steps(f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
+                                                     Frag (&fb)[2][kNI], const GEP_LDS char* cur, LA& la, LB& lb,
+                                                     GEP_LDS char* nxt, const KtSrc& src, int wave, int lane,
+                                                     int wm0, int wn0) {
+    if constexpr (S + 1 < kSteps) {
+      step<S & 1, (S < kWriteSteps), S * kChunksPerStep>(acc, fa, fb, cur, S + 1, la, lb, nxt, src, wave, lane,
+                                                         wm0, wn0);
+      first_steps<S + 1>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+    }
+  }
+
+  // k-tile kt, held in stage PAR (= kt & 1); fragments (kt, 0) are in buffer 0 and the
+  // staging registers hold k-tile kt+1. The first kWriteSteps steps write kt+1 into the
+  // other stage (free: its last reads were issued before the previous barrier) and reload
+  // the registers with kt+2. The barrier (after lgkmcnt(0): this wave's writes landed and
+  // its reads of stage PAR returned) comes before the last step, which reads (kt+1, 0).
   template <int PAR>
   static __device__ __forceinline__ void ktile(const KParams& p, const TileInfo& ti, LA& la, LB& lb,
                                                GEP_LDS char* smem, f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
                                                Frag (&fb)[2][kNI], int kt, int wave, int lane, int wm0, int wn0) {
-    const GEP_LDS char* st = smem + (kt % STAGES) * kStageBytes;
-    const GEP_LDS char* st1 = smem + ((kt + 1) % STAGES) * kStageBytes;
-    if constexpr (kSteps == 2) {
-      constexpr int SET = (PAR + 1) & 1;  // register set of k-tile kt+1 (and kt+3)
-      step<0, true, SET>(p, ti, la, lb, smem, acc, fa, fb, st, 1, kt + 1, kt + 3, wave, lane, wm0, wn0);
-      lds_barrier();
-      step<1, false, 0>(p, ti, la, lb, smem, acc, fa, fb, st1, 0, 0, 0, wave, lane, wm0, wn0);
-    } else {
-      constexpr int SET = PAR;  // register set of k-tile kt+2 (and kt+4)
-      lds_barrier();
-      step<PAR, true, SET>(p, ti, la, lb, smem, acc, fa, fb, st1, 0, kt + 2, kt + 4, wave, lane, wm0, wn0);
-    }
+    GEP_LDS char* cur = smem + PAR * kStageBytes;
+    GEP_LDS char* nxt = smem + (PAR ^ 1) * kStageBytes;
+    const KtSrc src = kt_src(p, ti, kt + 2);
+    first_steps(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+    lds_barrier();
+    step<1, false, 0>(acc, fa, fb, nxt, 0, la, lb, nxt, src, wave, lane, wm0, wn0);
   }
 
-  // Scale, add beta*C, activate, convert and store one kStripRows x kWN strip staged in LDS.
-  static __device__ __forceinline__ void epilogue_strip(const KParams& p, const float GEP_LDS* strip, int lane,
-                                                        int mrow0, int ncol0, int row_end, int l, float alpha,
-                                                        float beta) {
-    constexpr int kRowsPerIt = 64 / kStripChunks;
-    const int rr = lane / kStripChunks, q = lane % kStripChunks;
-    const int n = ncol0 + q * 4;
-    if (n >= p.N) return;
-    const int64_t c_lb = VARLEN ? 0 : (int64_t)l * p.sc;
-    const int64_t d_lb = VARLEN ? 0 : (int64_t)l * p.sd;
-    const int64_t p_lb = VARLEN ? 0 : (int64_t)l * p.sp;
-    const int cb = dt_bytes(p.c_dt), db = dt_bytes(p.d_dt), pb = dt_bytes(p.p_dt);
-#pragma unroll 1
-    for (int it = 0; it < kStripRows / kRowsPerIt; ++it) {
-      const int row = it * kRowsPerIt + rr;
-      const int m = mrow0 + row;
-      if (m >= row_end) break;
-      const f32x4 x = *(const f32x4 GEP_LDS*)(strip + row * kWN + ((q ^ (row & 7)) << 2));
-      float v[4] = {x[0] * alpha, x[1] * alpha, x[2] * alpha, x[3] * alpha};
-      if (p.c_dt != DT_NONE) {
-        float c[4];
-        load4((const char*)p.C + (c_lb + (int64_t)m * p.ldc + n) * cb, p.c_dt, c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
-      }
-      if (p.d_dt != DT_NONE) store4((char*)p.D + (d_lb + (int64_t)m * p.ldd + n) * db, p.d_dt, v);
-      if (p.p_dt != DT_NONE) {
-        float w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = apply_act(p.act, v[e]);
-        store4((char*)p.Post + (p_lb + (int64_t)m * p.ldp + n) * pb, p.p_dt, w);
-      }
-    }
-  }
-
+  // ---- epilogue -----------------------------------------------------------------------
   // Accumulator lane layout: for block (i, j) and register group g, lane l holds row
   // wm0 + 32i + (l % 32) and columns wn0 + 32j + 8g + 4(l / 32) + [0, 4).
-  static __device__ __forceinline__ void epilogue(const KParams& p, const TileInfo& ti,
-                                                  const f32x16 (&acc)[kMI][kNI], float GEP_LDS* region, int wave,
-                                                  int lane, int wm0, int wn0, float alpha, float beta) {
-    float GEP_LDS* strip = region + wave * kStripRows * kWN;
-    const int r16 = lane & 15;
-    const bool mine_lo = ((lane >> 4) & 1) == 0;  // lane holds rows 0..15 of its 32-row block
-#pragma unroll
-    for (int i = 0; i < kMI; ++i) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (mine_lo == (h == 0)) {
-#pragma unroll
-          for (int j = 0; j < kNI; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                               acc[i][j][4 * g + 3]};
-              const int q = j * 8 + 2 * g + (lane >> 5);
-              *(f32x4 GEP_LDS*)(strip + r16 * kWN + ((q ^ (r16 & 7)) << 2)) = v;
-            }
-        }
-        // LDS operations of one wave complete in order; keep the compiler from reordering
-        asm volatile("" ::: "memory");
-        epilogue_strip(p, strip, lane, ti.m0 + wm0 + i * 32 + h * 16, ti.n0 + wn0, ti.row_end, ti.l, alpha, beta);
-        asm volatile("" ::: "memory");
+  // Per pass of kBPP block rows, the wave writes its raw fp32 accumulators (straight from
+  // the accumulator registers) to a row-major buffer in its share of the idle ring, then
+  // reads them back 4 consecutive columns per lane, so that C loads and D / PostAct stores
+  // are row-contiguous: alpha, beta * C, the activation and the conversion run there.
+  static constexpr int kEpiRegion = kLdsBytes / 4;
+  static constexpr int kNC = kWN / 4;                              // 16-byte chunks per row
+  static constexpr int kBPP = (kEpiRegion / (32 * kWN * 4)) < kMI ? (kEpiRegion / (32 * kWN * 4)) : kMI;
+  static_assert(kBPP >= 1 && kMI % kBPP == 0, "epilogue passes must cover the wave tile");
+  static constexpr int kRPI = 64 / kNC;                            // rows per read instruction
+
+  // 16-byte-chunk swizzle of the row-major buffer: the 32 rows one fragment group writes,
+  // and the kNC chunks one row's lanes read, fall in distinct banks.
+  static __device__ __forceinline__ int okey(int row) {
+    if constexpr (kNC >= 16) return row & 15;
+    else return (row >> 1) & 7;
+  }
+
+  // alpha * x + beta * C, activation, conversion and stores of 4 consecutive outputs of row m
+  // (batch offsets already applied to the pointers).
+  static __device__ __forceinline__ void finish4(const KParams& p, const char* cp, char* dp, char* pp,
+                                                 const f32x4& x, float alpha, float beta) {
+    float v[4] = {x[0] * alpha, x[1] * alpha, x[2] * alpha, x[3] * alpha};
+    if (p.c_dt != DT_NONE) {
+      float c[4];
+      if (p.c_dt == DT_F32) {
+        const f32x4 y = *(const f32x4*)cp;
+        c[0] = y[0]; c[1] = y[1]; c[2] = y[2]; c[3] = y[3];
+      } else {
+        unpack4_16(p.c_dt, *(const uint2*)cp, c);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
+    }
+    if (p.d_dt == DT_F32) *(f32x4*)dp = f32x4{v[0], v[1], v[2], v[3]};
+    else if (p.d_dt != DT_NONE) *(uint2*)dp = pack4_16(p.d_dt, v);
+    if (p.p_dt != DT_NONE) {
+      float w[4];
+      switch (p.act) {
+        case ACT_RELU:
+          for (int e = 0; e < 4; ++e) w[e] = act_fn<ACT_RELU>(v[e]);
+          break;
+        case ACT_RELU_SQ:
+          for (int e = 0; e < 4; ++e) w[e] = act_fn<ACT_RELU_SQ>(v[e]);
+          break;
+        case ACT_GELU_TANH:
+          for (int e = 0; e < 4; ++e) w[e] = act_fn<ACT_GELU_TANH>(v[e]);
+          break;
+        case ACT_SILU:
+          for (int e = 0; e < 4; ++e) w[e] = act_fn<ACT_SILU>(v[e]);
+          break;
+        default:
+          for (int e = 0; e < 4; ++e) w[e] = v[e];
+      }
+      if (p.p_dt == DT_F32) *(f32x4*)pp = f32x4{w[0], w[1], w[2], w[3]};
+      else *(uint2*)pp = pack4_16(p.p_dt, w);
+    }
+  }
+
+  static __device__ __forceinline__ void epilogue(const KParams& p, const TileInfo& ti,
+                                                  const f32x16 (&acc)[kMI][kNI], GEP_LDS char* region, int lane,
+                                                  int wm0, int wn0, float alpha, float beta) {
+    const int h = lane >> 5;
+    const int row0 = ti.m0 + wm0, col0 = ti.n0 + wn0;
+    const int rows_valid = ti.row_end - row0, cols_valid = p.N - col0;
+    const int esc = dt_bytes(p.c_dt), esd = dt_bytes(p.d_dt), esp = dt_bytes(p.p_dt);
+    const char* cb = (const char*)p.C + ((VARLEN ? 0 : (int64_t)ti.l * p.sc) + (int64_t)row0 * p.ldc + col0) * esc;
+    char* db = (char*)p.D + ((VARLEN ? 0 : (int64_t)ti.l * p.sd) + (int64_t)row0 * p.ldd + col0) * esd;
+    char* pb = (char*)p.Post + ((VARLEN ? 0 : (int64_t)ti.l * p.sp) + (int64_t)row0 * p.ldp + col0) * esp;
+    const int rl = lane / kNC, c = lane % kNC;
+    const bool col_ok = 4 * c < cols_valid;
+#pragma unroll
+    for (int pass = 0; pass < kMI / kBPP; ++pass) {
+      // raw accumulators of kBPP block rows -> LDS
+#pragma unroll
+      for (int ii = 0; ii < kBPP; ++ii) {
+        const int lr = ii * 32 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < kNI; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& a = acc[pass * kBPP + ii][j];
+            const f32x4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+            const int q = 8 * j + 2 * g + h;
+            *(f32x4 GEP_LDS*)(region + lr * (kWN * 4) + ((q ^ okey(lr)) << 4)) = v;
+          }
+      }
+      // LDS operations of one wave complete in order; keep the compiler from reordering
+      asm volatile("" ::: "memory");
+      // row-contiguous: lane reads 4 columns of row r (kRPI rows per instruction)
+#pragma unroll 4
+      for (int r = rl; r < kBPP * 32; r += kRPI) {
+        const f32x4 x = *(const f32x4 GEP_LDS*)(region + r * (kWN * 4) + ((c ^ okey(r)) << 4));
+        const int m = pass * kBPP * 32 + r;
+        if (col_ok && m < rows_valid)
+          finish4(p, cb + ((int64_t)m * p.ldc + 4 * c) * esc, db + ((int64_t)m * p.ldd + 4 * c) * esd,
+                  pb + ((int64_t)m * p.ldp + 4 * c) * esp, x, alpha, beta);
+      }
+      asm volatile("" ::: "memory");
     }
   }
 
@@ -624,20 +681,22 @@ struct GemmKernel {
 
     const float alpha = p.alpha_ptr ? *p.alpha_ptr : p.alpha;
     const float beta = p.beta_ptr ? *p.beta_ptr : p.beta;
-    // k-tiles, run in pairs (the register sets alternate): an odd count gets one padding
-    // k-tile past K, whose loads read zeros and which adds nothing.
-    int nk = (p.K + kBK - 1) / kBK;
-    nk = (nk + 1) & ~1;
-    float GEP_LDS* epi_region = (float GEP_LDS*)(smem + STAGES * kStageBytes);
+    // k-tiles, run in pairs (the stages alternate): an odd count gets one more k-tile past
+    // K, whose loads read zeros and which adds nothing
+    const int nk = (((p.K + kBK - 1) / kBK) + 1) & ~1;
 
     LA la;
     LB lb;
     Frag fa[2][kMI], fb[2][kNI];
     TileInfo ti;
-    if (bb < T) {
-      ti = decode(p, bb, gstart);
-      prologue_loads(p, ti, la, lb, wave, lane);
-    }
+    // a tile's first k-tile goes into the staging registers as early as possible
+    auto begin_tile = [&](int t) {
+      ti = decode(p, t, gstart);
+      la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES, p.K);
+      lb.init(wave, lane, p.N - ti.n0, p.ldb * kES, p.K);
+      load_all(la, lb, kt_src(p, ti, 0));
+    };
+    if (bb < T) begin_tile(bb);
     int iter = 0;
     for (int t = bb; t < T; t += P, ++iter) {
       if (p.tile_log && iter < p.tile_log_iters && tid == 0) {
@@ -651,9 +710,11 @@ struct GemmKernel {
         for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
 
       if (nk > 0) {
-        prologue_stores(p, ti, la, lb, smem, wave, lane);
+        // the previous tile's epilogue strips are free; k-tile 0 -> stage 0, registers <- k-tile 1
         lds_barrier();
-        read_step(fa[0], fb[0], smem, 0, wm0, wn0, lane);
+        cycle_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 1), wave, lane);
+        lds_barrier();
+        read_all(fa[0], fb[0], smem, 0, wm0, wn0, lane);
         for (int kt = 0; kt < nk; kt += 2) {
           ktile<0>(p, ti, la, lb, smem, acc, fa, fb, kt, wave, lane, wm0, wn0);
           ktile<1>(p, ti, la, lb, smem, acc, fa, fb, kt + 1, wave, lane, wm0, wn0);
@@ -661,16 +722,12 @@ struct GemmKernel {
       }
 
       // ---- the next tile's first loads go in flight (into registers), then this tile's
-      // epilogue, in its own LDS region. The barrier ends every wave's reads of the ring,
-      // which the next tile's first LDS writes overwrite.
+      // epilogue, through strips in the ring. The barrier ends every wave's reads of the ring.
       lds_barrier();
       const TileInfo cur = ti;
       const int tnext = t + P;
-      if (tnext < T) {
-        ti = decode(p, tnext, gstart);
-        prologue_loads(p, ti, la, lb, wave, lane);
-      }
-      epilogue(p, cur, acc, epi_region, wave, lane, wm0, wn0, alpha, beta);
+      if (tnext < T) begin_tile(tnext);
+      epilogue(p, cur, acc, smem + wave * kEpiRegion, lane, wm0, wn0, alpha, beta);
     }
   }
 };

@@ -6,7 +6,6 @@
 
 namespace gep {
 
-constexpr int kStages = 2;
 
 // Workgroups per CU the kernel is built for: 256x256 tiles keep 256 accumulators per lane
 // (one workgroup per CU); 128x128 tiles fit two per CU.
@@ -15,7 +14,7 @@ constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
 
 template <int BM, int OP, int FA, int FB, bool AK, bool BK, bool VL>
 __global__ __launch_bounds__(256, wg_per_cu<BM>()) void gemm_persistent_kernel(const KParams p) {
-  GemmKernel<BM, BM, OP, FA, FB, AK, BK, VL, kStages>::run(p);
+  GemmKernel<BM, BM, OP, FA, FB, AK, BK, VL>::run(p);
 }
 
 template <int BM, int OP, int FA, int FB, bool AK, bool BK, bool VL>
