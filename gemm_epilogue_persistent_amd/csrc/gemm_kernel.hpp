@@ -49,6 +49,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------------------------
 // MFMA flavours. Frag = the per-lane operand registers of one 32-row fragment.
@@ -527,23 +528,108 @@ struct GemmKernel {
   // wm0 + 32i + (l % 32) and columns wn0 + 32j + 8g + 4(l / 32) + [0, 4).
   // Per pass of kBPP block rows, the wave writes its raw fp32 accumulators (straight from
   // the accumulator registers) to a row-major buffer in its share of the idle ring, then
-  // reads them back 4 consecutive columns per lane, so that C loads and D / PostAct stores
-  // are row-contiguous: alpha, beta * C, the activation and the conversion run there.
+  // reads them back 8 consecutive columns per lane, so that C loads and D / PostAct stores
+  // are 16-byte, row-contiguous accesses: alpha, beta * C, the activation and the
+  // conversion run there. Common type combinations (C / D / PostAct all bf16 or all f16)
+  // take a branch-free path with the C loads of a pass issued together; the others a
+  // generic one.
   static constexpr int kEpiRegion = kLdsBytes / 4;
-  static constexpr int kNC = kWN / 4;                              // 16-byte chunks per row
+  static constexpr int kNC8 = kWN / 8;                             // 8-column groups per row
   static constexpr int kBPP = (kEpiRegion / (32 * kWN * 4)) < kMI ? (kEpiRegion / (32 * kWN * 4)) : kMI;
   static_assert(kBPP >= 1 && kMI % kBPP == 0, "epilogue passes must cover the wave tile");
-  static constexpr int kRPI = 64 / kNC;                            // rows per read instruction
+  static constexpr int kRPI = 64 / kNC8;                           // rows per read instruction
+  static constexpr int kIt = kBPP * 32 / kRPI;                     // read instructions per pass
 
-  // 16-byte-chunk swizzle of the row-major buffer: the 32 rows one fragment group writes,
-  // and the kNC chunks one row's lanes read, fall in distinct banks.
-  static __device__ __forceinline__ int okey(int row) {
-    if constexpr (kNC >= 16) return row & 15;
-    else return (row >> 1) & 7;
+  // Byte offset of half `hf` (columns 8*c8 + 4*hf + [0, 4)) of row r in the wave's fp32
+  // buffer: the first halves of all groups fill the first half of the row, the second
+  // halves the second, each chunk index XOR-swizzled by the row. Acc-layout writes (32 rows,
+  // one group) and row reads (one or two rows, all groups) then fall in distinct banks.
+  static __device__ __forceinline__ int ebuf(int r, int c8, int hf) {
+    return r * (kWN * 4) + hf * (kWN * 2) + ((c8 ^ (r & (kNC8 - 1))) << 4);
   }
 
-  // alpha * x + beta * C, activation, conversion and stores of 4 consecutive outputs of row m
-  // (batch offsets already applied to the pointers).
+  template <int DT>
+  static __device__ __forceinline__ i32x4 pack8(const f32x8& v) {
+    if constexpr (DT == DT_BF16) return __builtin_bit_cast(i32x4, __builtin_convertvector(v, bf16x8));
+    else return __builtin_bit_cast(i32x4, __builtin_convertvector(v, f16x8));
+  }
+  template <int DT>
+  static __device__ __forceinline__ f32x8 unpack8(const i32x4& x) {
+    if constexpr (DT == DT_BF16) return __builtin_convertvector(__builtin_bit_cast(bf16x8, x), f32x8);
+    else return __builtin_convertvector(__builtin_bit_cast(f16x8, x), f32x8);
+  }
+  static __device__ __forceinline__ f32x8 act8(int act, const f32x8& v) {
+    f32x8 w;
+    switch (act) {
+      case ACT_RELU:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = act_fn<ACT_RELU>(v[e]);
+        break;
+      case ACT_RELU_SQ:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = act_fn<ACT_RELU_SQ>(v[e]);
+        break;
+      case ACT_GELU_TANH:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = act_fn<ACT_GELU_TANH>(v[e]);
+        break;
+      case ACT_SILU:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = act_fn<ACT_SILU>(v[e]);
+        break;
+      default:
+        w = v;
+    }
+    return w;
+  }
+
+  // Everything a pass needs about the wave's part of the output tile.
+  struct EpiArgs {
+    const char* cb;  // C, D, PostAct at the wave tile's first row and column
+    char* db;
+    char* pb;
+    int rows_valid, cols_valid;
+    float alpha, beta;
+  };
+
+  // Branch-free pass: C, D and PostAct (those present) all of type DT (bf16 or f16). The
+  // only branches are uniform ones around whole batches of C loads and around stores.
+  template <int DT>
+  static __device__ __forceinline__ void pass_fast(const KParams& p, const EpiArgs& ea, const GEP_LDS char* buf,
+                                                   int m0, int lane) {
+    constexpr int kCB = kIt < 4 ? kIt : 4;  // read instructions per batch of C loads
+    const int rl = lane / kNC8, c8 = lane % kNC8;
+    const bool col_ok = 8 * c8 < ea.cols_valid;
+    const bool hc = p.c_dt != DT_NONE, hd = p.d_dt != DT_NONE, hp = p.p_dt != DT_NONE;
+    const float beta = hc ? ea.beta : 0.f;
+#pragma unroll 1
+    for (int it0 = 0; it0 < kIt; it0 += kCB) {
+      i32x4 cv[kCB];
+#pragma unroll
+      for (int u = 0; u < kCB; ++u) cv[u] = i32x4{0, 0, 0, 0};
+      if (hc) {
+#pragma unroll
+        for (int u = 0; u < kCB; ++u) {
+          const int m = m0 + (it0 + u) * kRPI + rl;
+          if (col_ok && m < ea.rows_valid) cv[u] = *(const i32x4*)(ea.cb + ((int64_t)m * p.ldc + 8 * c8) * 2);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCB; ++u) {
+        const int r = (it0 + u) * kRPI + rl, m = m0 + r;
+        const f32x4 x0 = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, 0));
+        const f32x4 x1 = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, 1));
+        f32x8 v = f32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]} * ea.alpha;
+        v += beta * unpack8<DT>(cv[u]);  // + 0 when there is no C
+        if (col_ok && m < ea.rows_valid) {
+          if (hd) *(i32x4*)(ea.db + ((int64_t)m * p.ldd + 8 * c8) * 2) = pack8<DT>(v);
+          if (hp) *(i32x4*)(ea.pb + ((int64_t)m * p.ldp + 8 * c8) * 2) = pack8<DT>(act8(p.act, v));
+        }
+      }
+    }
+  }
+
+  // Four outputs of the generic pass (any C / D / PostAct types), at 4-element pointers.
   static __device__ __forceinline__ void finish4(const KParams& p, const char* cp, char* dp, char* pp,
                                                  const f32x4& x, float alpha, float beta) {
     float v[4] = {x[0] * alpha, x[1] * alpha, x[2] * alpha, x[3] * alpha};
@@ -561,25 +647,29 @@ struct GemmKernel {
     if (p.d_dt == DT_F32) *(f32x4*)dp = f32x4{v[0], v[1], v[2], v[3]};
     else if (p.d_dt != DT_NONE) *(uint2*)dp = pack4_16(p.d_dt, v);
     if (p.p_dt != DT_NONE) {
-      float w[4];
-      switch (p.act) {
-        case ACT_RELU:
-          for (int e = 0; e < 4; ++e) w[e] = act_fn<ACT_RELU>(v[e]);
-          break;
-        case ACT_RELU_SQ:
-          for (int e = 0; e < 4; ++e) w[e] = act_fn<ACT_RELU_SQ>(v[e]);
-          break;
-        case ACT_GELU_TANH:
-          for (int e = 0; e < 4; ++e) w[e] = act_fn<ACT_GELU_TANH>(v[e]);
-          break;
-        case ACT_SILU:
-          for (int e = 0; e < 4; ++e) w[e] = act_fn<ACT_SILU>(v[e]);
-          break;
-        default:
-          for (int e = 0; e < 4; ++e) w[e] = v[e];
-      }
+      const f32x8 w8 = act8(p.act, f32x8{v[0], v[1], v[2], v[3], 0.f, 0.f, 0.f, 0.f});
+      float w[4] = {w8[0], w8[1], w8[2], w8[3]};
       if (p.p_dt == DT_F32) *(f32x4*)pp = f32x4{w[0], w[1], w[2], w[3]};
       else *(uint2*)pp = pack4_16(p.p_dt, w);
+    }
+  }
+
+  static __device__ __forceinline__ void pass_generic(const KParams& p, const EpiArgs& ea, const GEP_LDS char* buf,
+                                                      int m0, int lane) {
+    const int rl = lane / kNC8, c8 = lane % kNC8;
+    const int esc = dt_bytes(p.c_dt), esd = dt_bytes(p.d_dt), esp = dt_bytes(p.p_dt);
+    const bool col_ok = 8 * c8 < ea.cols_valid;
+#pragma unroll 1
+    for (int it = 0; it < kIt; ++it) {
+      const int r = it * kRPI + rl, m = m0 + r;
+      if (!(col_ok && m < ea.rows_valid)) continue;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 x = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, hf));
+        const int n = 8 * c8 + 4 * hf;
+        finish4(p, ea.cb + ((int64_t)m * p.ldc + n) * esc, ea.db + ((int64_t)m * p.ldd + n) * esd,
+                ea.pb + ((int64_t)m * p.ldp + n) * esp, x, ea.alpha, ea.beta);
+      }
     }
   }
 
@@ -588,40 +678,44 @@ struct GemmKernel {
                                                   int wm0, int wn0, float alpha, float beta) {
     const int h = lane >> 5;
     const int row0 = ti.m0 + wm0, col0 = ti.n0 + wn0;
-    const int rows_valid = ti.row_end - row0, cols_valid = p.N - col0;
     const int esc = dt_bytes(p.c_dt), esd = dt_bytes(p.d_dt), esp = dt_bytes(p.p_dt);
-    const char* cb = (const char*)p.C + ((VARLEN ? 0 : (int64_t)ti.l * p.sc) + (int64_t)row0 * p.ldc + col0) * esc;
-    char* db = (char*)p.D + ((VARLEN ? 0 : (int64_t)ti.l * p.sd) + (int64_t)row0 * p.ldd + col0) * esd;
-    char* pb = (char*)p.Post + ((VARLEN ? 0 : (int64_t)ti.l * p.sp) + (int64_t)row0 * p.ldp + col0) * esp;
-    const int rl = lane / kNC, c = lane % kNC;
-    const bool col_ok = 4 * c < cols_valid;
-#pragma unroll
+    EpiArgs ea;
+    ea.cb = (const char*)p.C + ((VARLEN ? 0 : (int64_t)ti.l * p.sc) + (int64_t)row0 * p.ldc + col0) * esc;
+    ea.db = (char*)p.D + ((VARLEN ? 0 : (int64_t)ti.l * p.sd) + (int64_t)row0 * p.ldd + col0) * esd;
+    ea.pb = (char*)p.Post + ((VARLEN ? 0 : (int64_t)ti.l * p.sp) + (int64_t)row0 * p.ldp + col0) * esp;
+    ea.rows_valid = ti.row_end - row0;
+    ea.cols_valid = p.N - col0;
+    ea.alpha = alpha;
+    ea.beta = beta;
+    // one output type for C, D and PostAct (those present), 16-bit: the branch-free path
+    const int ot = p.d_dt != DT_NONE ? p.d_dt : p.p_dt;
+    const bool same = (p.c_dt == DT_NONE || p.c_dt == ot) && (p.p_dt == DT_NONE || p.p_dt == ot);
+    const int path = !same ? 0 : (ot == DT_BF16 ? 1 : (ot == DT_F16 ? 2 : 0));
+#pragma unroll 1
     for (int pass = 0; pass < kMI / kBPP; ++pass) {
-      // raw accumulators of kBPP block rows -> LDS
+      // raw accumulators of kBPP block rows -> LDS (the accumulator index must be literal)
 #pragma unroll
-      for (int ii = 0; ii < kBPP; ++ii) {
-        const int lr = ii * 32 + (lane & 31);
+      for (int pc = 0; pc < kMI / kBPP; ++pc) {
+        if (pc != pass) continue;
 #pragma unroll
-        for (int j = 0; j < kNI; ++j)
+        for (int ii = 0; ii < kBPP; ++ii) {
+          const int lr = ii * 32 + (lane & 31);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x16& a = acc[pass * kBPP + ii][j];
-            const f32x4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-            const int q = 8 * j + 2 * g + h;
-            *(f32x4 GEP_LDS*)(region + lr * (kWN * 4) + ((q ^ okey(lr)) << 4)) = v;
-          }
+          for (int j = 0; j < kNI; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x16& a = acc[pc * kBPP + ii][j];
+              const f32x4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+              *(f32x4 GEP_LDS*)(region + ebuf(lr, 4 * j + g, h)) = v;
+            }
+        }
       }
       // LDS operations of one wave complete in order; keep the compiler from reordering
       asm volatile("" ::: "memory");
-      // row-contiguous: lane reads 4 columns of row r (kRPI rows per instruction)
-#pragma unroll 4
-      for (int r = rl; r < kBPP * 32; r += kRPI) {
-        const f32x4 x = *(const f32x4 GEP_LDS*)(region + r * (kWN * 4) + ((c ^ okey(r)) << 4));
-        const int m = pass * kBPP * 32 + r;
-        if (col_ok && m < rows_valid)
-          finish4(p, cb + ((int64_t)m * p.ldc + 4 * c) * esc, db + ((int64_t)m * p.ldd + 4 * c) * esd,
-                  pb + ((int64_t)m * p.ldp + 4 * c) * esp, x, alpha, beta);
-      }
+      const int m0 = pass * kBPP * 32;
+      if (path == 1) pass_fast<DT_BF16>(p, ea, region, m0, lane);
+      else if (path == 2) pass_fast<DT_F16>(p, ea, region, m0, lane);
+      else pass_generic(p, ea, region, m0, lane);
       asm volatile("" ::: "memory");
     }
   }
@@ -721,13 +815,14 @@ struct GemmKernel {
         }
       }
 
-      // ---- the next tile's first loads go in flight (into registers), then this tile's
-      // epilogue, through strips in the ring. The barrier ends every wave's reads of the ring.
+      // ---- this tile's epilogue, through per-wave buffers in the ring (the barrier ends every
+      // wave's reads of it), then the next tile's first loads. (Issued before the epilogue,
+      // those loads would gain nothing: a wait on them after the epilogue's stores also
+      // waits for the stores, and their registers would crowd the epilogue.)
       lds_barrier();
-      const TileInfo cur = ti;
+      epilogue(p, ti, acc, smem + wave * kEpiRegion, lane, wm0, wn0, alpha, beta);
       const int tnext = t + P;
       if (tnext < T) begin_tile(tnext);
-      epilogue(p, cur, acc, smem + wave * kEpiRegion, lane, wm0, wn0, alpha, beta);
     }
   }
 };
