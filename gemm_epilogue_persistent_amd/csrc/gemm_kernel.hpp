@@ -169,6 +169,17 @@ struct TileLoader {
     reg[Q] = __builtin_amdgcn_raw_buffer_load_b128(rs, k0 + Q * kDK < klim ? offv[Q] : kOOB, 0, 0);
   }
 
+  // Global -> LDS directly (buffer_load_dwordx4 ... lds), chunk Q: the wave's 64 lanes
+  // fill the 1 KB block q*4+wave of the tile at `lds` in lane order, the layout the
+  // register path writes.
+  template <int Q>
+  __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, int k0, GEP_LDS char* lds, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the builtin exists for the gfx950 pass only
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GEP_LDS void*)(lds + (Q * 4 + wave) * 1024), 16,
+                                             k0 + Q * kDK < klim ? offv[Q] : kOOB, 0, 0, 0);
+#endif
+  }
+
   // Registers -> LDS (tile base `lds`), chunk Q.
   template <int Q>
   __device__ __forceinline__ void store(GEP_LDS char* lds, int wave, int lane) const {
@@ -284,6 +295,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// As lds_barrier, after this wave's global -> LDS transfers (buffer_load ... lds) have
+// landed too: after it, every wave's transfers issued before it are visible.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ------------------------------------------------------------------------------------
 // Tile scheduler: linear tile id -> (m_blk, n_blk) inside one batch / group
 // ------------------------------------------------------------------------------------
@@ -341,7 +360,11 @@ struct GemmKernel {
   // register chunks of one k-tile, written to LDS (and reloaded) over the first kWriteSteps
   // MFMA steps, kCPF chunks next to each fragment read
   static constexpr int kChunksPerKt = LA::kInstr + LB::kInstr;
-  static constexpr int kWriteSteps = kSteps >= 4 ? 2 : 1;
+  // kDMA: k-tiles go global -> LDS directly (buffer_load ... lds), all chunks of k-tile
+  // kt+2 issued in the last MFMA step of k-tile kt; else through the staging registers
+  // over the first kWriteSteps steps
+  static constexpr bool kDMA = kES == 1;  // measured: faster for fp8 (frees the staging registers), slower for 16-bit
+  static constexpr int kWriteSteps = kDMA ? 1 : (kSteps >= 4 ? 2 : 1);
   static constexpr int kChunksPerStep = kChunksPerKt / kWriteSteps;
   static constexpr int kCPF = kChunksPerStep / kFrags;
   static constexpr int kMPF = kMfmaPerStep / kFrags;       // MFMAs per fragment slot
@@ -361,8 +384,8 @@ struct GemmKernel {
       __builtin_amdgcn_sched_group_barrier(0x008, kMPF, 0);                     // MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, F < kMI ? kRA : kRB, 0);      // LDS reads
       if constexpr (WR) {
-        __builtin_amdgcn_sched_group_barrier(0x200, kCPF, 0);                   // LDS writes
-        __builtin_amdgcn_sched_group_barrier(0x020, kCPF, 0);                   // VMEM loads
+        if constexpr (!kDMA) __builtin_amdgcn_sched_group_barrier(0x200, kCPF, 0);  // LDS writes
+        __builtin_amdgcn_sched_group_barrier(0x020, kCPF, 0);                        // VMEM loads
       }
       sched_step<WR, F + 1>();
     }
@@ -465,6 +488,18 @@ struct GemmKernel {
     }
   }
 
+  // Global -> LDS transfers of register-chunk positions [C0, C0 + N) of the k-tile `src`
+  // into the stage at `st`.
+  template <int C0, int N>
+  static __device__ __forceinline__ void dma_chunks(const LA& la, const LB& lb, GEP_LDS char* st, const KtSrc& src,
+                                                    int wave) {
+    if constexpr (N > 0) {
+      if constexpr (C0 < LA::kInstr) la.template dma<C0>(src.a, src.k0, st, wave);
+      else lb.template dma<C0 - LA::kInstr>(src.b, src.k0, st + kABytes, wave);
+      dma_chunks<C0 + 1, N - 1>(la, lb, st, src, wave);
+    }
+  }
+
   // Fragment slot F of a step: read fragment F (A fragments first) of k-step s into `fa`/
   // `fb`, then (WR) cycle kCPF register chunks starting at C0 + F * kCPF.
   template <bool WR, int C0, int F = 0>
@@ -474,7 +509,10 @@ struct GemmKernel {
     if constexpr (F < kFrags) {
       if constexpr (F < kMI) fa[F] = read_frag<A_K, BM, Op>(rd, wm0 + F * 32, s, lane);
       else fb[F - kMI] = read_frag<B_K, BN, Op>(rd + kABytes, wn0 + (F - kMI) * 32, s, lane);
-      if constexpr (WR) cycle_chunks<C0 + F * kCPF, kCPF>(la, lb, wr, src, wave, lane);
+      if constexpr (WR) {
+        if constexpr (kDMA) dma_chunks<C0 + F * kCPF, kCPF>(la, lb, wr, src, wave);
+        else cycle_chunks<C0 + F * kCPF, kCPF>(la, lb, wr, src, wave, lane);
+      }
       slots<WR, C0, F + 1>(fa, fb, rd, s, wm0, wn0, la, lb, wr, src, wave, lane);
     }
   }
@@ -494,15 +532,15 @@ struct GemmKernel {
   // Steps S .. kSteps-2 of a k-tile (stage `cur`): step S runs the MFMAs of k-step S on
   // buffer S & 1 and reads k-step S+1; the first kWriteSteps steps also cycle their share of
   // the register chunks through the stage `nxt`.
-  template <int S = 0>
+  template <int S = 0, bool WRITES = true>
   static __device__ __forceinline__ void first_steps(f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
                                                      Frag (&fb)[2][kNI], const GEP_LDS char* cur, LA& la, LB& lb,
                                                      GEP_LDS char* nxt, const KtSrc& src, int wave, int lane,
                                                      int wm0, int wn0) {
     if constexpr (S + 1 < kSteps) {
-      step<S & 1, (S < kWriteSteps), S * kChunksPerStep>(acc, fa, fb, cur, S + 1, la, lb, nxt, src, wave, lane,
-                                                         wm0, wn0);
-      first_steps<S + 1>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+      step<S & 1, (WRITES && S < kWriteSteps), S * kChunksPerStep>(acc, fa, fb, cur, S + 1, la, lb, nxt, src,
+                                                                   wave, lane, wm0, wn0);
+      first_steps<S + 1, WRITES>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
     }
   }
 
@@ -518,9 +556,17 @@ struct GemmKernel {
     GEP_LDS char* cur = smem + PAR * kStageBytes;
     GEP_LDS char* nxt = smem + (PAR ^ 1) * kStageBytes;
     const KtSrc src = kt_src(p, ti, kt + 2);
-    first_steps(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
-    lds_barrier();
-    step<1, false, 0>(acc, fa, fb, nxt, 0, la, lb, nxt, src, wave, lane, wm0, wn0);
+    if constexpr (kDMA) {
+      // stage PAR^1 (k-tile kt+1) was filled by transfers issued in the last step of k-tile
+      // kt-1; k-tile kt+2 goes into stage PAR once its last fragments have been read
+      first_steps<0, false>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+      dma_barrier();
+      step<1, true, 0>(acc, fa, fb, nxt, 0, la, lb, cur, src, wave, lane, wm0, wn0);
+    } else {
+      first_steps(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+      lds_barrier();
+      step<1, false, 0>(acc, fa, fb, nxt, 0, la, lb, nxt, src, wave, lane, wm0, wn0);
+    }
   }
 
   // ---- epilogue -----------------------------------------------------------------------
@@ -788,7 +834,7 @@ struct GemmKernel {
       ti = decode(p, t, gstart);
       la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES, p.K);
       lb.init(wave, lane, p.N - ti.n0, p.ldb * kES, p.K);
-      load_all(la, lb, kt_src(p, ti, 0));
+      if constexpr (!kDMA) load_all(la, lb, kt_src(p, ti, 0));
     };
     if (bb < T) begin_tile(bb);
     int iter = 0;
@@ -804,10 +850,18 @@ struct GemmKernel {
         for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
 
       if (nk > 0) {
-        // the previous tile's epilogue strips are free; k-tile 0 -> stage 0, registers <- k-tile 1
+        // the previous tile's epilogue buffers are free
         lds_barrier();
-        cycle_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 1), wave, lane);
-        lds_barrier();
+        if constexpr (kDMA) {
+          // k-tiles 0 and 1 -> stages 0 and 1
+          dma_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 0), wave);
+          dma_chunks<0, kChunksPerKt>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);
+          dma_barrier();
+        } else {
+          // k-tile 0 -> stage 0, registers <- k-tile 1
+          cycle_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 1), wave, lane);
+          lds_barrier();
+        }
         read_all(fa[0], fb[0], smem, 0, wm0, wn0, lane);
         for (int kt = 0; kt < nk; kt += 2) {
           ktile<0>(p, ti, la, lb, smem, acc, fa, fb, kt, wave, lane, wm0, wn0);
@@ -819,7 +873,10 @@ struct GemmKernel {
       // wave's reads of it), then the next tile's first loads. (Issued before the epilogue,
       // those loads would gain nothing: a wait on them after the epilogue's stores also
       // waits for the stores, and their registers would crowd the epilogue.)
-      lds_barrier();
+      // (global -> LDS transfers of the padding k-tiles past K must land before the ring is
+      // reused)
+      if constexpr (kDMA) dma_barrier();
+      else lds_barrier();
       epilogue(p, ti, acc, smem + wave * kEpiRegion, lane, wm0, wn0, alpha, beta);
       const int tnext = t + P;
       if (tnext < T) begin_tile(tnext);
