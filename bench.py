@@ -50,7 +50,7 @@ def algorithmic_bytes(inp):
     return a + b + mn * (es[inp.c_dt] + es[inp.d_dt] + es[inp.post_dt])
 
 
-def setup(name):
+def setup(name, **tuning):
     import torch
     import workloads as W
     from gemm_epilogue_persistent_amd import Plan
@@ -60,7 +60,7 @@ def setup(name):
     D = out_like(inp, inp.d_dt) if inp.d_dt != "none" else None
     P = out_like(inp, inp.post_dt) if inp.post_dt != "none" else None
     cu = torch.from_numpy(inp.cu_seqlens).to("cuda") if inp.varlen else None
-    plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu)
+    plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu, **tuning)
     args = (A, B, C, D, P, None, None, cu)
     return inp, plan, args
 

@@ -120,34 +120,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 // Loader of one operand's k-tile: ROWS rows (M or N) by kRowBytes of K, staged through
 // VGPRs: each lane loads kInstr 16-byte chunks (buffer_load_dwordx4) and later writes them
-// with ds_write_b128 to fixed LDS positions (block q*4+wave of 1 KB, lane*16 inside it).
+// with ds_write_b128 to fixed LDS positions (block q*NW+wave of 1 KB, lane*16 inside it).
 // The global address of a lane is the inverse of the LDS swizzle, so LDS writes are
 // contiguous and conflict-free, and the 8 (K-major) or 32/16 (M/N-major) lanes that fill
 // one LDS row read one contiguous 128/512/256-byte run of global memory.
-template <int ROWS, bool KMAJ, int ES>
+template <int ROWS, bool KMAJ, int ES, int NW, bool PAD>
 struct TileLoader {
-  static constexpr int kTileBytes = ROWS * kRowBytes;
-  static constexpr int kInstr = kTileBytes / 1024 / 4;
+  // K-major rows in LDS: kRowBytes of K, either padded to kPitch (PAD; 9 16-byte slots
+  // per row, an odd count, so the 16 rows of a fragment read phase hit 16 distinct slots)
+  // or XOR-swizzled (kswz; the layout global -> LDS transfers can produce).
+  static constexpr int kPitch = (KMAJ && PAD) ? kRowBytes + 16 : kRowBytes;
+  static constexpr int kTileBytes = ROWS * kPitch;  // LDS bytes of one k-tile
+  static constexpr int kInstr = ROWS * kRowBytes / 1024 / NW;
   static constexpr int kCPR = ROWS * ES / 16;                  // MN-major: chunks per k-row
   static constexpr int kKPI = KMAJ ? 1 : 1024 / (ROWS * ES);   // MN-major: k-rows per instruction
-  static_assert(kInstr >= 1, "tile too small for 4 waves");
+  static_assert(kInstr >= 1, "tile too small for the waves");
   uint32_t offv[kInstr];   // byte offset of this lane's chunk in the k-tile, or kOOB when the
                            // row / column chunk lies outside the operand
   int32_t klim;            // chunk q exists while k0 + q * kDK < klim (K minus the chunk's
                            // k offset in the k-tile)
   i32x4 reg[kInstr];       // staging registers
   // k offset between consecutive chunks of a lane: K-major chunks of one lane share their
-  // k offset (the swizzle key repeats every 32 rows); M/N-major ones step 4*kKPI k-rows
-  static constexpr int kDK = KMAJ ? 0 : 4 * kKPI;
+  // k offset (the swizzle key repeats every 16 rows); M/N-major ones step NW*kKPI k-rows
+  static constexpr int kDK = KMAJ ? 0 : NW * kKPI;
 
   // rows_valid: rows of this tile that exist (K-major) or MN elements that exist (MN-major).
   __device__ __forceinline__ void init(int wave, int lane, int rows_valid, int64_t ld_bytes, int K) {
 #pragma unroll
     for (int q = 0; q < kInstr; ++q) {
-      const int blk = q * 4 + wave;
+      const int blk = q * NW + wave;
       if constexpr (KMAJ) {
         const int row = blk * (1024 / kRowBytes) + lane / kChunks;
-        const int c = (lane % kChunks) ^ kswz(row);
+        const int c = PAD ? lane % kChunks : (lane % kChunks) ^ kswz(row);
         offv[q] = row < rows_valid ? (uint32_t)(row * ld_bytes + c * 16) : kOOB;
       } else {
         const int krow = blk * kKPI + lane / kCPR;
@@ -155,7 +159,9 @@ struct TileLoader {
         offv[q] = c * (16 / ES) < rows_valid ? (uint32_t)(krow * ld_bytes + c * 16) : kOOB;
       }
     }
-    if constexpr (KMAJ) {
+    if constexpr (KMAJ && PAD) {
+      klim = K - (lane % kChunks) * (16 / ES);
+    } else if constexpr (KMAJ) {
       klim = K - (((lane % kChunks) ^ kswz(wave * (1024 / kRowBytes) + lane / kChunks)) * (16 / ES));
     } else {
       klim = K - (wave * kKPI + lane / kCPR);
@@ -170,12 +176,13 @@ struct TileLoader {
   }
 
   // Global -> LDS directly (buffer_load_dwordx4 ... lds), chunk Q: the wave's 64 lanes
-  // fill the 1 KB block q*4+wave of the tile at `lds` in lane order, the layout the
+  // fill the 1 KB block Q*NW+wave of the tile at `lds` in lane order, the layout the
   // register path writes.
   template <int Q>
   __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, int k0, GEP_LDS char* lds, int wave) const {
+    static_assert(!(KMAJ && PAD), "transfers fill whole 1 KB blocks: no row padding");
 #if defined(__HIP_DEVICE_COMPILE__)  // the builtin exists for the gfx950 pass only
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GEP_LDS void*)(lds + (Q * 4 + wave) * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GEP_LDS void*)(lds + (Q * NW + wave) * 1024), 16,
                                              k0 + Q * kDK < klim ? offv[Q] : kOOB, 0, 0, 0);
 #endif
   }
@@ -183,7 +190,11 @@ struct TileLoader {
   // Registers -> LDS (tile base `lds`), chunk Q.
   template <int Q>
   __device__ __forceinline__ void store(GEP_LDS char* lds, int wave, int lane) const {
-    *(GEP_LDS i32x4*)(lds + (Q * 4 + wave) * 1024 + lane * 16) = reg[Q];
+    if constexpr (KMAJ && PAD)
+      *(GEP_LDS i32x4*)(lds + ((Q * NW + wave) * (1024 / kRowBytes) + lane / kChunks) * kPitch +
+                        (lane % kChunks) * 16) = reg[Q];
+    else
+      *(GEP_LDS i32x4*)(lds + (Q * NW + wave) * 1024 + lane * 16) = reg[Q];
   }
 };
 
@@ -192,13 +203,13 @@ template <bool KMAJ, int ES>
 constexpr int reads_per_frag() { return KMAJ ? (ES == 2 ? 1 : 2) : 2; }
 
 // Fragment reader: rows [r0, r0+32) of a tile, MFMA k-step s of the k-tile.
-template <bool KMAJ, int ROWS, class Op>
+template <bool KMAJ, int ROWS, class Op, bool PAD>
 __device__ __forceinline__ typename Op::Frag read_frag(const GEP_LDS char* tile, int r0, int s, int lane) {
   using Frag = typename Op::Frag;
   if constexpr (KMAJ) {
     const int row = r0 + (lane & 31);
-    const int sw = kswz(row);
-    const GEP_LDS char* rp = tile + row * kRowBytes;
+    const int sw = PAD ? 0 : kswz(row);
+    const GEP_LDS char* rp = tile + row * (PAD ? kRowBytes + 16 : kRowBytes);
     if constexpr (Op::kES == 2) {
       const int c = s * 2 + (lane >> 5);
       return *(const GEP_LDS i32x4*)(rp + ((c ^ sw) << 4));
@@ -340,52 +351,66 @@ struct TileInfo {
 };
 
 
-template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, bool VARLEN>
+template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, bool VARLEN, int NW>
 struct GemmKernel {
+  // NW wave64s in a 2 x (NW/2) grid over the output tile
+  static constexpr int kThreads = NW * 64;
   using Op = Mfma<OP, FA, FB>;
   using Frag = typename Op::Frag;
   static constexpr int kES = Op::kES;
   static constexpr int kBK = kRowBytes / kES;             // K elements per k-tile
   static constexpr int kSteps = kBK / Op::kKStep;          // MFMA k-steps per k-tile (4 or 2)
-  static constexpr int kWM = BM / 2, kWN = BN / 2;         // per-wave output block
+  static constexpr int kWM = BM / 2, kWN = BN / (NW / 2);  // per-wave output block
   static constexpr int kMI = kWM / 32, kNI = kWN / 32;     // 32x32 MFMA blocks per wave
-  using LA = TileLoader<BM, A_K, kES>;
-  using LB = TileLoader<BN, B_K, kES>;
+  // kDMA: k-tiles go global -> LDS directly (buffer_load ... lds), all chunks of k-tile
+  // kt+2 issued in the last MFMA step of k-tile kt; else through the staging registers
+  // over the first kWriteSteps steps. Measured: direct transfers win for fp8 (they free the
+  // staging registers, which fp8's 32-byte fragments need) and lose for 16-bit operands
+  // (batched M/N-major -30%).
+  static constexpr bool kDMA = kES == 1;
+  // Padded K-major rows (PAD) cost the register path two-way bank conflicts on its LDS
+  // writes: measured 3% slower than the XOR swizzle with 4 waves. They only pay where
+  // the per-step address registers of the swizzle do not fit (8 waves).
+  static constexpr bool kPadRows = !kDMA && NW == 8;
+  using LA = TileLoader<BM, A_K, kES, NW, kPadRows>;
+  using LB = TileLoader<BN, B_K, kES, NW, kPadRows>;
   static constexpr int kABytes = LA::kTileBytes, kBBytes = LB::kTileBytes;
-  static constexpr int kStageBytes = kABytes + kBBytes;
-  static constexpr int kLdsBytes = 2 * kStageBytes;
+  // Ring layout [A stage 0 | A stage 1 | B stage 0 | B stage 1]: a stage is named by its A
+  // tile (at s * kABytes) and its B tile sits kBOff further. The offsets between stages and
+  // fragments then fit the 16-bit immediate of the LDS instructions, so one address
+  // register per (k-step, operand) serves both stages and every fragment.
+  static constexpr int kStageBytes = kABytes > kBBytes ? kABytes : kBBytes;  // stage s at s * kStageBytes
+  static constexpr int kBOff = 2 * kStageBytes;
+  static constexpr int kLdsBytes = 4 * kStageBytes;
   static constexpr int kFrags = kMI + kNI;
   static constexpr int kMfmaPerStep = kMI * kNI;
   static constexpr int kRA = reads_per_frag<A_K, kES>(), kRB = reads_per_frag<B_K, kES>();
   // register chunks of one k-tile, written to LDS (and reloaded) over the first kWriteSteps
   // MFMA steps, kCPF chunks next to each fragment read
   static constexpr int kChunksPerKt = LA::kInstr + LB::kInstr;
-  // kDMA: k-tiles go global -> LDS directly (buffer_load ... lds), all chunks of k-tile
-  // kt+2 issued in the last MFMA step of k-tile kt; else through the staging registers
-  // over the first kWriteSteps steps
-  static constexpr bool kDMA = kES == 1;  // measured: faster for fp8 (frees the staging registers), slower for 16-bit
   static constexpr int kWriteSteps = kDMA ? 1 : (kSteps >= 4 ? 2 : 1);
   static constexpr int kChunksPerStep = kChunksPerKt / kWriteSteps;
-  static constexpr int kCPF = kChunksPerStep / kFrags;
-  static constexpr int kMPF = kMfmaPerStep / kFrags;       // MFMAs per fragment slot
+  // fragment slot f carries MFMAs [mlo(f), mlo(f+1)) and register chunks [clo(f), clo(f+1))
+  static constexpr int mlo(int f) { return f * kMfmaPerStep / kFrags; }
+  static constexpr int clo(int f) { return f * kChunksPerStep / kFrags; }
   static_assert(kSteps % 2 == 0, "a k-tile ends on fragment buffer 0");
-  static_assert(kChunksPerKt % kWriteSteps == 0 && kChunksPerStep % kFrags == 0 && kCPF >= 1,
-                "register chunks must spread evenly over the fragment slots");
-  static_assert(kMfmaPerStep % kFrags == 0 && kMPF >= 1, "MFMAs must spread evenly over the fragment slots");
+  static_assert(kChunksPerKt % kWriteSteps == 0, "register chunks must spread evenly over the write steps");
+  static_assert(kMfmaPerStep >= kFrags, "every fragment slot needs an MFMA");
 
-  // ---- scheduling hints: one slot per fragment, each carrying kMPF MFMAs, the fragment's
-  // LDS reads and (WR) kCPF LDS writes and global loads, in that order. Program order
+  // ---- scheduling hints: one slot per fragment, each carrying its MFMAs, the fragment's
+  // LDS reads and (WR) its register chunks' LDS writes and global loads, in that order. Program order
   // already interleaves the memory operations the same way (the compiler keeps LDS reads
   // and writes it cannot prove disjoint in program order). The builtin needs literal
   // arguments, hence the compile-time recursion.
   template <bool WR, int F = 0>
   static __device__ __forceinline__ void sched_step() {
     if constexpr (F < kFrags) {
-      __builtin_amdgcn_sched_group_barrier(0x008, kMPF, 0);                     // MFMAs
+      constexpr int nm = mlo(F + 1) - mlo(F), nc = clo(F + 1) - clo(F);
+      __builtin_amdgcn_sched_group_barrier(0x008, nm, 0);                       // MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, F < kMI ? kRA : kRB, 0);      // LDS reads
-      if constexpr (WR) {
-        if constexpr (!kDMA) __builtin_amdgcn_sched_group_barrier(0x200, kCPF, 0);  // LDS writes
-        __builtin_amdgcn_sched_group_barrier(0x020, kCPF, 0);                        // VMEM loads
+      if constexpr (WR && nc > 0) {
+        if constexpr (!kDMA) __builtin_amdgcn_sched_group_barrier(0x200, nc, 0);  // LDS writes
+        __builtin_amdgcn_sched_group_barrier(0x020, nc, 0);                       // VMEM loads
       }
       sched_step<WR, F + 1>();
     }
@@ -402,9 +427,9 @@ struct GemmKernel {
   static __device__ __forceinline__ void read_all(Frag (&fa)[kMI], Frag (&fb)[kNI], const GEP_LDS char* st, int s,
                                                   int wm0, int wn0, int lane) {
 #pragma unroll
-    for (int i = 0; i < kMI; ++i) fa[i] = read_frag<A_K, BM, Op>(st, wm0 + i * 32, s, lane);
+    for (int i = 0; i < kMI; ++i) fa[i] = read_frag<A_K, BM, Op, kPadRows>(st, wm0 + i * 32, s, lane);
 #pragma unroll
-    for (int j = 0; j < kNI; ++j) fb[j] = read_frag<B_K, BN, Op>(st + kABytes, wn0 + j * 32, s, lane);
+    for (int j = 0; j < kNI; ++j) fb[j] = read_frag<B_K, BN, Op, kPadRows>(st + kBOff, wn0 + j * 32, s, lane);
   }
 
   static __device__ __forceinline__ TileInfo decode(const KParams& p, int t, const int32_t* gstart) {
@@ -466,7 +491,7 @@ struct GemmKernel {
       la.template store<C>(wr, wave, lane);
       la.template load<C>(src.a, src.k0);
     } else {
-      lb.template store<C - LA::kInstr>(wr + kABytes, wave, lane);
+      lb.template store<C - LA::kInstr>(wr + kBOff, wave, lane);
       lb.template load<C - LA::kInstr>(src.b, src.k0);
     }
   }
@@ -495,38 +520,81 @@ struct GemmKernel {
                                                     int wave) {
     if constexpr (N > 0) {
       if constexpr (C0 < LA::kInstr) la.template dma<C0>(src.a, src.k0, st, wave);
-      else lb.template dma<C0 - LA::kInstr>(src.b, src.k0, st + kABytes, wave);
+      else lb.template dma<C0 - LA::kInstr>(src.b, src.k0, st + kBOff, wave);
       dma_chunks<C0 + 1, N - 1>(la, lb, st, src, wave);
     }
   }
 
   // Fragment slot F of a step: read fragment F (A fragments first) of k-step s into `fa`/
-  // `fb`, then (WR) cycle kCPF register chunks starting at C0 + F * kCPF.
+  // `fb`, then (WR) cycle register chunks C0 + [clo(F), clo(F+1)).
   template <bool WR, int C0, int F = 0>
   static __device__ __forceinline__ void slots(Frag (&fa)[kMI], Frag (&fb)[kNI], const GEP_LDS char* rd, int s,
                                                int wm0, int wn0, LA& la, LB& lb, GEP_LDS char* wr,
                                                const KtSrc& src, int wave, int lane) {
     if constexpr (F < kFrags) {
-      if constexpr (F < kMI) fa[F] = read_frag<A_K, BM, Op>(rd, wm0 + F * 32, s, lane);
-      else fb[F - kMI] = read_frag<B_K, BN, Op>(rd + kABytes, wn0 + (F - kMI) * 32, s, lane);
+      if constexpr (F < kMI) fa[F] = read_frag<A_K, BM, Op, kPadRows>(rd, wm0 + F * 32, s, lane);
+      else fb[F - kMI] = read_frag<B_K, BN, Op, kPadRows>(rd + kBOff, wn0 + (F - kMI) * 32, s, lane);
       if constexpr (WR) {
-        if constexpr (kDMA) dma_chunks<C0 + F * kCPF, kCPF>(la, lb, wr, src, wave);
-        else cycle_chunks<C0 + F * kCPF, kCPF>(la, lb, wr, src, wave, lane);
+        if constexpr (kDMA) dma_chunks<C0 + clo(F), clo(F + 1) - clo(F)>(la, lb, wr, src, wave);
+        else cycle_chunks<C0 + clo(F), clo(F + 1) - clo(F)>(la, lb, wr, src, wave, lane);
       }
       slots<WR, C0, F + 1>(fa, fb, rd, s, wm0, wn0, la, lb, wr, src, wave, lane);
     }
   }
 
+  // ---- rolling A fragments (kRoll): one A buffer, re-read row by row. Slot i runs the
+  // MFMAs of accumulator row i, then reads A fragment i of the next k-step into the same
+  // registers (their last reader has issued), B fragment i of the next k-step (i < kNI) into
+  // the other B buffer, then cycles its register chunks. Saves kMI fragment registers, which
+  // lets two waves share a SIMD.
+  static constexpr bool kRoll = NW == 8;
+  static constexpr int rlo(int i) { return i * kChunksPerStep / kMI; }
+  template <bool WR, int I = 0>
+  static __device__ __forceinline__ void sched_roll() {
+    if constexpr (I < kMI) {
+      constexpr int nc = rlo(I + 1) - rlo(I);
+      __builtin_amdgcn_sched_group_barrier(0x008, kNI, 0);                              // MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, kRA + (I < kNI ? kRB : 0), 0);        // LDS reads
+      if constexpr (WR && nc > 0) {
+        if constexpr (!kDMA) __builtin_amdgcn_sched_group_barrier(0x200, nc, 0);         // LDS writes
+        __builtin_amdgcn_sched_group_barrier(0x020, nc, 0);                              // VMEM loads
+      }
+      sched_roll<WR, I + 1>();
+    }
+  }
+  template <int CUR, bool WR, int C0, int I = 0>
+  static __device__ __forceinline__ void roll_slots(f32x16 (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[2][kNI],
+                                                    const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
+                                                    const KtSrc& src, int wave, int lane, int wm0, int wn0) {
+    if constexpr (I < kMI) {
+#pragma unroll
+      for (int j = 0; j < kNI; ++j) acc[I][j] = Op::mma(fb[CUR][j], fa[I], acc[I][j]);
+      fa[I] = read_frag<A_K, BM, Op, kPadRows>(rd, wm0 + I * 32, s, lane);
+      if constexpr (I < kNI) fb[CUR ^ 1][I] = read_frag<B_K, BN, Op, kPadRows>(rd + kBOff, wn0 + I * 32, s, lane);
+      if constexpr (WR) {
+        if constexpr (kDMA) dma_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave);
+        else cycle_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave, lane);
+      }
+      roll_slots<CUR, WR, C0, I + 1>(acc, fa, fb, rd, s, la, lb, wr, src, wave, lane, wm0, wn0);
+    }
+  }
+
   // One MFMA step: MFMAs on fragment buffer CUR while the fragments of k-step s of the stage
   // at `rd` are read into the other buffer; WR: register chunks [C0, C0 + kChunksPerStep)
-  // are written to the stage at `wr` and reloaded from `src`.
+  // are written to the stage at `wr` and reloaded from `src`. (kRoll: A in buffer 0 only.)
   template <int CUR, bool WR, int C0>
   static __device__ __forceinline__ void step(f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI], Frag (&fb)[2][kNI],
                                               const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
                                               const KtSrc& src, int wave, int lane, int wm0, int wn0) {
-    slots<WR, C0>(fa[CUR ^ 1], fb[CUR ^ 1], rd, s, wm0, wn0, la, lb, wr, src, wave, lane);
-    mma_step(acc, fa[CUR], fb[CUR]);
-    sched_step<WR>();
+    if constexpr (kRoll) {
+      static_assert(kNI <= kMI, "B fragments are read in the first kNI slots");
+      roll_slots<CUR, WR, C0>(acc, fa[0], fb, rd, s, la, lb, wr, src, wave, lane, wm0, wn0);
+      sched_roll<WR>();
+    } else {
+      slots<WR, C0>(fa[CUR ^ 1], fb[CUR ^ 1], rd, s, wm0, wn0, la, lb, wr, src, wave, lane);
+      mma_step(acc, fa[CUR], fb[CUR]);
+      sched_step<WR>();
+    }
   }
 
   // Steps S .. kSteps-2 of a k-tile (stage `cur`): step S runs the MFMAs of k-step S on
@@ -579,7 +647,7 @@ struct GemmKernel {
   // conversion run there. Common type combinations (C / D / PostAct all bf16 or all f16)
   // take a branch-free path with the C loads of a pass issued together; the others a
   // generic one.
-  static constexpr int kEpiRegion = kLdsBytes / 4;
+  static constexpr int kEpiRegion = kLdsBytes / NW;
   static constexpr int kNC8 = kWN / 8;                             // 8-column groups per row
   static constexpr int kBPP = (kEpiRegion / (32 * kWN * 4)) < kMI ? (kEpiRegion / (32 * kWN * 4)) : kMI;
   static_assert(kBPP >= 1 && kMI % kBPP == 0, "epilogue passes must cover the wave tile");
@@ -771,7 +839,14 @@ struct GemmKernel {
     GEP_LDS char* smem = (GEP_LDS char*)smem_raw;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
-    const int wm0 = (wave >> 1) * kWM, wn0 = (wave & 1) * kWN;
+    if constexpr (NW == 8) {
+      // With two waves per SIMD a wave has 256 registers in all. An explicit AGPR operand
+      // makes the compiler split them 128 / 128 and keep the accumulators in AGPRs;
+      // otherwise it assumes no AGPRs and spills the 128 accumulators plus the rest of
+      // the loop state out of 256 VGPRs.
+      asm volatile("; accumulators live in AGPRs" ::"a"(0.f));
+    }
+    const int wm0 = (wave & 1) * kWM, wn0 = (wave >> 1) * kWN;
 
     const int P = p.P;
     const int bid = blockIdx.x;
@@ -782,9 +857,9 @@ struct GemmKernel {
     int T = p.T;
     if constexpr (VARLEN) {
       __shared__ int32_t s_start[kMaxVarlenGroups + 1];
-      __shared__ int32_t s_part[256];
+      __shared__ int32_t s_part[kThreads];
       const int G = p.L;
-      constexpr int kPer = (kMaxVarlenGroups + 255) / 256;
+      constexpr int kPer = (kMaxVarlenGroups + kThreads - 1) / kThreads;
       int32_t local[kPer];
       int32_t sum = 0;
 #pragma unroll
@@ -800,8 +875,8 @@ struct GemmKernel {
       }
       s_part[tid] = sum;
       __syncthreads();
-      // inclusive scan of the 256 partial sums (Hillis-Steele)
-      for (int off = 1; off < 256; off <<= 1) {
+      // inclusive scan of the partial sums (Hillis-Steele)
+      for (int off = 1; off < kThreads; off <<= 1) {
         const int32_t add = tid >= off ? s_part[tid - off] : 0;
         __syncthreads();
         s_part[tid] += add;
@@ -813,7 +888,7 @@ struct GemmKernel {
         const int g = tid * kPer + q;
         if (g < G) s_start[g] = excl + local[q];
       }
-      if (tid == 255) s_start[G] = s_part[255];
+      if (tid == kThreads - 1) s_start[G] = s_part[kThreads - 1];
       __syncthreads();
       gstart = s_start;
       T = s_start[G];
