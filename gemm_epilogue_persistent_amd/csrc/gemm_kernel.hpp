@@ -706,25 +706,25 @@ struct GemmKernel {
     float alpha, beta;
   };
 
-  // Branch-free pass: C, D and PostAct (those present) all of type DT (bf16 or f16). The
-  // only branches are uniform ones around whole batches of C loads and around stores.
-  template <int DT>
+  // Branch-free pass: C (HC), D and PostAct (those present) all of type DT (bf16 or f16).
+  // Without C the pass issues no global load, so no wait in it covers its own stores (a
+  // wait on a load after a store is a vmcnt(0): loads and stores share the counter); with
+  // C the loads of a batch of kCB row groups are issued together, one wait per batch.
+  template <int DT, bool HC>
   static __device__ __forceinline__ void pass_fast(const KParams& p, const EpiArgs& ea, const GEP_LDS char* buf,
                                                    int m0, int lane) {
-    constexpr int kCB = kIt < 4 ? kIt : 4;  // read instructions per batch of C loads
+    constexpr int kCB = kIt < 4 ? kIt : 4;  // row groups per batch
     const int rl = lane / kNC8, c8 = lane % kNC8;
     const bool col_ok = 8 * c8 < ea.cols_valid;
-    const bool hc = p.c_dt != DT_NONE, hd = p.d_dt != DT_NONE, hp = p.p_dt != DT_NONE;
-    const float beta = hc ? ea.beta : 0.f;
+    const bool hd = p.d_dt != DT_NONE, hp = p.p_dt != DT_NONE;
 #pragma unroll 1
     for (int it0 = 0; it0 < kIt; it0 += kCB) {
-      i32x4 cv[kCB];
-#pragma unroll
-      for (int u = 0; u < kCB; ++u) cv[u] = i32x4{0, 0, 0, 0};
-      if (hc) {
+      [[maybe_unused]] i32x4 cv[kCB];
+      if constexpr (HC) {
 #pragma unroll
         for (int u = 0; u < kCB; ++u) {
           const int m = m0 + (it0 + u) * kRPI + rl;
+          cv[u] = i32x4{0, 0, 0, 0};
           if (col_ok && m < ea.rows_valid) cv[u] = *(const i32x4*)(ea.cb + ((int64_t)m * p.ldc + 8 * c8) * 2);
         }
       }
@@ -734,7 +734,7 @@ struct GemmKernel {
         const f32x4 x0 = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, 0));
         const f32x4 x1 = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, 1));
         f32x8 v = f32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]} * ea.alpha;
-        v += beta * unpack8<DT>(cv[u]);  // + 0 when there is no C
+        if constexpr (HC) v += ea.beta * unpack8<DT>(cv[u]);
         if (col_ok && m < ea.rows_valid) {
           if (hd) *(i32x4*)(ea.db + ((int64_t)m * p.ldd + 8 * c8) * 2) = pack8<DT>(v);
           if (hp) *(i32x4*)(ea.pb + ((int64_t)m * p.ldp + 8 * c8) * 2) = pack8<DT>(act8(p.act, v));
@@ -827,8 +827,13 @@ struct GemmKernel {
       // LDS operations of one wave complete in order; keep the compiler from reordering
       asm volatile("" ::: "memory");
       const int m0 = pass * kBPP * 32;
-      if (path == 1) pass_fast<DT_BF16>(p, ea, region, m0, lane);
-      else if (path == 2) pass_fast<DT_F16>(p, ea, region, m0, lane);
+      if (path == 1) {
+        if (p.c_dt != DT_NONE) pass_fast<DT_BF16, true>(p, ea, region, m0, lane);
+        else pass_fast<DT_BF16, false>(p, ea, region, m0, lane);
+      } else if (path == 2) {
+        if (p.c_dt != DT_NONE) pass_fast<DT_F16, true>(p, ea, region, m0, lane);
+        else pass_fast<DT_F16, false>(p, ea, region, m0, lane);
+      }
       else pass_generic(p, ea, region, m0, lane);
       asm volatile("" ::: "memory");
     }
