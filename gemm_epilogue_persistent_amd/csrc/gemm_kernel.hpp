@@ -365,9 +365,10 @@ struct GemmKernel {
   // kDMA: k-tiles go global -> LDS directly (buffer_load ... lds), all chunks of k-tile
   // kt+2 issued in the last MFMA step of k-tile kt; else through the staging registers
   // over the first kWriteSteps steps. Measured: direct transfers win for fp8 (they free the
-  // staging registers, which fp8's 32-byte fragments need) and lose for 16-bit operands
-  // (batched M/N-major -30%).
-  static constexpr bool kDMA = kES == 1;
+  // staging registers, which fp8's 32-byte fragments need) and for 16-bit operands with
+  // 8 waves (the staging registers do not fit next to two waves' accumulators); with 4
+  // waves they lose for 16-bit operands (batched M/N-major -30%).
+  static constexpr bool kDMA = kES == 1 || NW == 8;
   // Padded K-major rows (PAD) cost the register path two-way bank conflicts on its LDS
   // writes: measured 3% slower than the XOR swizzle with 4 waves. They only pay where
   // the per-step address registers of the swizzle do not fit (8 waves).

@@ -11,21 +11,23 @@ namespace gep {
 // over a CU's waves (one workgroup per CU); 128x128 tiles fit two per CU.
 template <int BM>
 constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
-// Waves per workgroup. The kernel also runs with 8 waves (two per SIMD, 128x64 accumulators
-// each); measured on the 8192^3 bf16, varlen-M and batched M/N-major workloads, 4 waves
-// were as fast or faster (8 waves lost ~30% on varlen-M), so every kernel uses 4.
-template <int BM, int OP>
-constexpr int waves() { return 4; }
+// Waves per workgroup. Dense 16-bit K-major x K-major 256x256 kernels run 8 waves (two per
+// SIMD, 128x64 accumulators each) with global -> LDS transfers: measured +2% on the 8192^3
+// GEMM and +4% on the 4096^3 GEMM with C and GELU. Every other kernel runs 4: with 8 waves
+// the varlen-M kernel lost ~30% and transfers slowed the M/N-major one by ~30%.
+template <int BM, int OP, bool AK, bool BK, bool VL>
+constexpr int waves() { return (BM == 256 && OP != OP_FP8 && AK && BK && !VL) ? 8 : 4; }
 
 template <int BM, int OP, int FA, int FB, bool AK, bool BK, bool VL>
-__global__ __launch_bounds__((waves<BM, OP>() * 64), (wg_per_cu<BM>())) void gemm_persistent_kernel(const KParams p) {
-  GemmKernel<BM, BM, OP, FA, FB, AK, BK, VL, waves<BM, OP>()>::run(p);
+__global__ __launch_bounds__((waves<BM, OP, AK, BK, VL>() * 64), (wg_per_cu<BM>())) void gemm_persistent_kernel(
+    const KParams p) {
+  GemmKernel<BM, BM, OP, FA, FB, AK, BK, VL, waves<BM, OP, AK, BK, VL>()>::run(p);
 }
 
 template <int BM, int OP, int FA, int FB, bool AK, bool BK, bool VL>
 hipError_t launch_one(const KParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_persistent_kernel<BM, OP, FA, FB, AK, BK, VL>), dim3(p.P), dim3(waves<BM, OP>() * 64), 0,
-                     s, p);
+  hipLaunchKernelGGL((gemm_persistent_kernel<BM, OP, FA, FB, AK, BK, VL>), dim3(p.P),
+                     dim3(waves<BM, OP, AK, BK, VL>() * 64), 0, s, p);
   return hipGetLastError();
 }
 
