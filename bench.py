@@ -31,7 +31,7 @@ def source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemm_epilogue_persistent_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
+        if f.endswith((".hip", ".hpp", ".cpp")) and f != "probe.hip":  # the probe is not the GEMM
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -79,6 +79,35 @@ def time_plan(plan, args, steps, warmup):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms per launch
+
+
+def mfma_ceiling(dtype, peak, reps=3):
+    """The library's MFMA rate probe: pure MFMA loops on uniform [-1, 1) operands held in
+    registers, one 4-wave workgroup per CU, no memory traffic. Returns the sustained rate and
+    the shader clock it ran at (cycles over the 100 MHz real-time counter)."""
+    import statistics
+    import torch
+    from gemm_epilogue_persistent_amd import probe_mfma
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
+    iters = 20000 if dtype == "bf16" else 10000
+    flop_iter = 16 * 2 * 32 * 32 * (16 if dtype == "bf16" else 64)
+    stream = torch.cuda.current_stream()
+    best = None
+    for _ in range(reps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        probe_mfma(dtype, iters, 1111, cus, out)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        h = out.view(cus, 2).cpu().tolist()
+        mhz = statistics.median(c / (r / 100.0) for c, r in h if r > 0)
+        tflops = flop_iter * iters * 4 * cus / (ms * 1e-3) / 1e12
+        if best is None or tflops > best["tflops"]:
+            best = {"tflops": round(tflops, 1), "clock_mhz": round(mhz), "frac_of_peak": round(tflops / peak, 4)}
+    return best
 
 
 def cpu_baseline(inp, budget_s=15.0):
@@ -130,6 +159,7 @@ def main():
     ap.add_argument("--workload", default=PRIMARY)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for traffic counters)")
@@ -174,6 +204,12 @@ def main():
                       "pct_of_peak": round(100 * tflops / peak, 2)},
            "roofline": roof}
     del args, plan
+    if not a.no_ceiling:
+        # the practical MFMA ceiling on full-entropy data at the clock the part sustains
+        ceil = {d: mfma_ceiling(d, PEAK_TFLOPS[d]) for d in ("bf16", "e4m3")}
+        out["mfma_ceiling"] = ceil
+        c = ceil["e4m3" if inp.a_dt in ("e4m3", "e5m2") else "bf16"]
+        roof["frac_of_mfma_ceiling"] = round(tflops / c["tflops"], 4)
     if not a.no_secondary:
         sec = {}
         for name in SECONDARY:
