@@ -383,6 +383,8 @@ struct GemmKernel {
   static constexpr int kStageBytes = kABytes > kBBytes ? kABytes : kBBytes;  // stage s at s * kStageBytes
   static constexpr int kBOff = 2 * kStageBytes;
   static constexpr int kLdsBytes = 4 * kStageBytes;
+  // varlen group table (tile offsets of the groups, scan partials) past the ring
+  static constexpr int kVarlenLds = (kMaxVarlenGroups + 1 + kThreads) * 4;
   static constexpr int kFrags = kMI + kNI;
   static constexpr int kMfmaPerStep = kMI * kNI;
   static constexpr int kRA = reads_per_frag<A_K, kES>(), kRB = reads_per_frag<B_K, kES>();
@@ -841,7 +843,10 @@ struct GemmKernel {
   }
 
   static __device__ __forceinline__ void run(const KParams& p) {
-    __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes];
+    // One LDS object: the varlen group table sits past the ring. (With a second LDS array in
+    // the kernel the compiler no longer separates fragment reads from pending global -> LDS
+    // transfers and waits for all of them before every read.)
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes + (VARLEN ? kVarlenLds : 0)];
     GEP_LDS char* smem = (GEP_LDS char*)smem_raw;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
@@ -862,8 +867,8 @@ struct GemmKernel {
     [[maybe_unused]] int32_t* gstart = nullptr;
     int T = p.T;
     if constexpr (VARLEN) {
-      __shared__ int32_t s_start[kMaxVarlenGroups + 1];
-      __shared__ int32_t s_part[kThreads];
+      int32_t* s_start = (int32_t*)(smem_raw + kLdsBytes);
+      int32_t* s_part = s_start + kMaxVarlenGroups + 1;
       const int G = p.L;
       constexpr int kPer = (kMaxVarlenGroups + kThreads - 1) / kThreads;
       int32_t local[kPer];

@@ -11,12 +11,13 @@ namespace gep {
 // over a CU's waves (one workgroup per CU); 128x128 tiles fit two per CU.
 template <int BM>
 constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
-// Waves per workgroup. Dense 16-bit K-major x K-major 256x256 kernels run 8 waves (two per
-// SIMD, 128x64 accumulators each) with global -> LDS transfers: measured +2% on the 8192^3
-// GEMM and +4% on the 4096^3 GEMM with C and GELU. Every other kernel runs 4: with 8 waves
-// the varlen-M kernel lost ~30% and transfers slowed the M/N-major one by ~30%.
+// Waves per workgroup. 16-bit K-major x K-major 256x256 kernels (dense and varlen-M) run 8
+// waves (two per SIMD, 128x64 accumulators each) with global -> LDS transfers: measured +2%
+// on the 8192^3 GEMM, +4% on the 4096^3 GEMM with C and GELU, +0.5-2.5% on varlen-M (its
+// epilogue halves; the store drain moves into the next tile's first wait). Every other kernel
+// runs 4: transfers slowed the M/N-major one by ~30%.
 template <int BM, int OP, bool AK, bool BK, bool VL>
-constexpr int waves() { return (BM == 256 && OP != OP_FP8 && AK && BK && !VL) ? 8 : 4; }
+constexpr int waves() { return (BM == 256 && OP != OP_FP8 && AK && BK) ? 8 : 4; }
 
 template <int BM, int OP, int FA, int FB, bool AK, bool BK, bool VL>
 __global__ __launch_bounds__((waves<BM, OP, AK, BK, VL>() * 64), (wg_per_cu<BM>())) void gemm_persistent_kernel(
