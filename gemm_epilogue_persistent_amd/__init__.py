@@ -60,7 +60,8 @@ def _bstride(t):
 
 
 def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none",
-             varlen=False, tile=None, group_m=0, max_ctas=0, xcd_remap=0):
+             varlen=False, tile=None, group_m=0, max_ctas=0, xcd_remap=0,
+             tail_split=0):
     """Build the gemm_desc for these tensors (no GPU work)."""
     d = _abi.GemmDesc()
     if varlen:
@@ -97,7 +98,7 @@ def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none"
     d.varlen_m = int(varlen)
     if tile is not None:
         d.tile_m, d.tile_n = tile
-    d.group_m, d.max_ctas, d.xcd_remap = group_m, max_ctas, xcd_remap
+    d.group_m, d.max_ctas, d.xcd_remap, d.tail_split = group_m, max_ctas, xcd_remap, tail_split
     return d
 
 

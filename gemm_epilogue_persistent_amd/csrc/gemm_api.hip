@@ -32,6 +32,14 @@ static gemm_status current_cus(int32_t* cus) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+static hipError_t launch_key(const KernelKey& key, const KParams& k, hipStream_t s) {
+  switch (key.op) {
+    case OP_F16: return launch_f16(key, k, s);
+    case OP_BF16: return launch_bf16(key, k, s);
+    default: return launch_fp8(key, k, s);
+  }
+}
+
 static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
                             void* Post, const float* alpha_dev, const float* beta_dev, const int32_t* cu,
                             int32_t* tile_log, int32_t max_iters, void* stream) {
@@ -64,12 +72,34 @@ static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B,
   if (st != GEMM_OK) return st;
   k.P = grid_size(plan, cus);
 
+  // Split tail (see tail_split in the header): grid of the quarter-tile launch, 0 for none.
+  int32_t p_tail = 0;
+  if (plan->tail_split && !tile_log) {
+    int64_t cap = 2 * (int64_t)cus;  // 128x128 kernels run two workgroups per CU
+    if (plan->max_ctas > 0 && plan->max_ctas < cap) cap = plan->max_ctas;
+    if (plan->varlen) {
+      // the device knows T; launch only if T can exceed one round at all
+      const int64_t t_max = ((int64_t)plan->base.M / plan->tile_m + 1 + plan->L) * plan->base.tn;
+      if (t_max > k.P) p_tail = (int32_t)cap;
+    } else {
+      const int64_t rem = plan->T % k.P;
+      if (plan->T > k.P && rem > 0 && 2 * rem <= k.P) p_tail = (int32_t)(4 * rem < cap ? 4 * rem : cap);
+    }
+  }
+  if (p_tail > 0) {
+    k.tail = 1;
+    k.P_big = k.P;
+  }
+
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  switch (plan->key.op) {
-    case OP_F16: e = launch_f16(plan->key, k, s); break;
-    case OP_BF16: e = launch_bf16(plan->key, k, s); break;
-    default: e = launch_fp8(plan->key, k, s); break;
+  hipError_t e = launch_key(plan->key, k, s);
+  if (e == hipSuccess && p_tail > 0) {
+    KParams kt = k;
+    kt.tail = 2;
+    kt.P = p_tail;
+    KernelKey key = plan->key;
+    key.tile = 1;
+    e = launch_key(key, kt, s);
   }
   if (e != hipSuccess) return fail(GEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   clear_error();

@@ -435,7 +435,14 @@ struct GemmKernel {
     for (int j = 0; j < kNI; ++j) fb[j] = read_frag<B_K, BN, Op, kPadRows>(st + kBOff, wn0 + j * 32, s, lane);
   }
 
-  static __device__ __forceinline__ TileInfo decode(const KParams& p, int t, const int32_t* gstart) {
+  // Work item u of this launch -> output tile. Tiles are numbered in the map's tiling (MT x
+  // (BN * MT / BM)): BM itself, or twice BM for the quarter tiles of a split tail (p.tail == 2,
+  // item u = quarter (u & 3) of map tile t_lo + (u >> 2); quarter q covers rows
+  // (q & 1) * BM and columns (q >> 1) * BN of it, and may lie wholly outside the output).
+  static __device__ __forceinline__ TileInfo decode(const KParams& p, int u, const int32_t* gstart, int t_lo) {
+    const bool quarter = p.tail == 2;
+    const int MT = quarter ? 2 * BM : BM, NT = quarter ? 2 * BN : BN;
+    const int t = quarter ? t_lo + (u >> 2) : u;
     TileInfo ti;
     uint32_t mb, nb;
     int row_base;
@@ -448,7 +455,7 @@ struct GemmKernel {
       ti.l = lo;
       row_base = p.cu_seqlens[lo];
       ti.row_end = p.cu_seqlens[lo + 1];
-      const uint32_t tmg = (uint32_t)((ti.row_end - row_base + BM - 1) / BM);
+      const uint32_t tmg = (uint32_t)((ti.row_end - row_base + MT - 1) / MT);
       raster(p, (uint32_t)(t - gstart[lo]), tmg, mb, nb);
     } else {
       uint32_t ll, r;
@@ -460,8 +467,12 @@ struct GemmKernel {
     }
     ti.mb = (int)mb;
     ti.nb = (int)nb;
-    ti.m0 = row_base + (int)mb * BM;
-    ti.n0 = (int)nb * BN;
+    ti.m0 = row_base + (int)mb * MT;
+    ti.n0 = (int)nb * NT;
+    if (quarter) {
+      ti.m0 += (u & 1) * BM;
+      ti.n0 += ((u >> 1) & 1) * BN;
+    }
     const int64_t a_lb = VARLEN ? 0 : (int64_t)ti.l * p.sa;
     const int64_t b_lb = (int64_t)ti.l * p.sb;
     const int64_t a_off = (a_lb + (A_K ? (int64_t)ti.m0 * p.lda : (int64_t)ti.m0)) * kES;
@@ -863,8 +874,9 @@ struct GemmKernel {
     const int bid = blockIdx.x;
     const int bb = (p.xcd_remap && (P & 7) == 0) ? (bid & 7) * (P >> 3) + (bid >> 3) : bid;
 
-    // ---- varlen: tile offsets of the groups, in LDS
+    // ---- varlen: tile offsets of the groups (in map tiles), in LDS
     [[maybe_unused]] int32_t* gstart = nullptr;
+    [[maybe_unused]] const int MT = p.tail == 2 ? 2 * BM : BM;
     int T = p.T;
     if constexpr (VARLEN) {
       int32_t* s_start = (int32_t*)(smem_raw + kLdsBytes);
@@ -879,7 +891,7 @@ struct GemmKernel {
         int32_t tiles = 0;
         if (g < G) {
           const int rows = p.cu_seqlens[g + 1] - p.cu_seqlens[g];
-          tiles = ((rows + BM - 1) / BM) * p.tn;
+          tiles = ((rows + MT - 1) / MT) * p.tn;
         }
         local[q] = sum;
         sum += tiles;
@@ -904,6 +916,20 @@ struct GemmKernel {
       gstart = s_start;
       T = s_start[G];
     }
+    // Split tail: when the last round of map tiles is partial and at most half full, a second
+    // launch (tail == 2, BM x BN kernel over the map of 2BM x 2BN tiles) takes it as quarter
+    // tiles, and the first launch (tail == 1) stops before it. Both decide from T alone.
+    int t_lo = 0, U = T;
+    if (p.tail != 0) {
+      const int rem = T % p.P_big;
+      const bool split = T > p.P_big && rem > 0 && 2 * rem <= p.P_big;
+      if (p.tail == 1) {
+        U = split ? T - rem : T;
+      } else {
+        t_lo = T - rem;
+        U = split ? 4 * rem : 0;
+      }
+    }
 
     const float alpha = p.alpha_ptr ? *p.alpha_ptr : p.alpha;
     const float beta = p.beta_ptr ? *p.beta_ptr : p.beta;
@@ -917,14 +943,18 @@ struct GemmKernel {
     TileInfo ti;
     // a tile's first k-tile goes into the staging registers as early as possible
     auto begin_tile = [&](int t) {
-      ti = decode(p, t, gstart);
+      ti = decode(p, t, gstart, t_lo);
       la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES, p.K);
       lb.init(wave, lane, p.N - ti.n0, p.ldb * kES, p.K);
       if constexpr (!kDMA) load_all(la, lb, kt_src(p, ti, 0));
     };
-    if (bb < T) begin_tile(bb);
+    if (bb < U) begin_tile(bb);
     int iter = 0;
-    for (int t = bb; t < T; t += P, ++iter) {
+    for (int t = bb; t < U; t += P, ++iter) {
+      if (ti.m0 >= ti.row_end || ti.n0 >= p.N) {  // a quarter tile wholly outside the output
+        if (t + P < U) begin_tile(t + P);
+        continue;
+      }
       if (p.tile_log && iter < p.tile_log_iters && tid == 0) {
         int32_t* e = p.tile_log + ((int64_t)bid * p.tile_log_iters + iter) * 4;
         e[0] = ti.mb; e[1] = ti.nb; e[2] = ti.l; e[3] = t;
@@ -965,7 +995,7 @@ struct GemmKernel {
       else lds_barrier();
       epilogue(p, ti, acc, smem + wave * kEpiRegion, lane, wm0, wn0, alpha, beta);
       const int tnext = t + P;
-      if (tnext < T) begin_tile(tnext);
+      if (tnext < U) begin_tile(tnext);
     }
   }
 };

@@ -37,6 +37,8 @@ struct KParams {
   int32_t P;        // workgroups in the grid
   int32_t log2G;    // raster group size G = 1 << log2G
   int32_t xcd_remap;
+  int32_t tail;     // 0: the whole map; 1: all but a split tail; 2: the split tail's quarter tiles
+  int32_t P_big;    // tail != 0: grid of the first launch (the map's round size)
   FastDiv fd_mn;    // tm * tn
   FastDiv fd_Gtn;   // G * tn
   FastDiv fd_tail[1 << kMaxGroupLog2];  // index w: divisor w (1 <= w < G); [0] unused
@@ -71,4 +73,5 @@ struct gemm_plan {
   int32_t max_ctas;
   int32_t varlen;
   int32_t L;          // groups (varlen) or batches
+  int32_t tail_split; // 1: gemm_run may split the last partial round into quarter tiles
 };

@@ -116,6 +116,7 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
     return fail(GEMM_ERR_INVALID_ARG, "group_m must be a power of two in [1, 16]");
   if (d.max_ctas < 0) return fail(GEMM_ERR_INVALID_ARG, "max_ctas < 0");
   if (d.xcd_remap < -1 || d.xcd_remap > 1) return fail(GEMM_ERR_INVALID_ARG, "xcd_remap must be -1, 0 or 1");
+  if (d.tail_split < -1 || d.tail_split > 1) return fail(GEMM_ERR_INVALID_ARG, "tail_split must be -1, 0 or 1");
   if (d.varlen_m && d.L > kMaxVarlenGroups)
     return fail(GEMM_ERR_UNSUPPORTED, "varlen-M supports at most %d groups", kMaxVarlenGroups);
 
@@ -248,6 +249,9 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
     k.fd_mn = make_fastdiv((uint32_t)std::max<int64_t>(1, tm * tn));
   }
   k.xcd_remap = d.xcd_remap == -1 ? 0 : 1;
+  k.tail = 0;
+  k.P_big = 0;
+  p->tail_split = (d.tail_split != -1 && key.tile == 0) ? 1 : 0;
   p->max_ctas = d.max_ctas;
   p->varlen = d.varlen_m;
   p->L = d.L;

@@ -102,7 +102,15 @@ typedef enum {
  *   tile_m, tile_n  output tile per workgroup; supported pairs: 256x256, 128x128.
  *   group_m         raster group size G of the tile map, power of two in [1, 16], default 8.
  *   max_ctas        cap on the persistent grid size.
- *   xcd_remap       -1: off, 0: default (on), 1: on. See gemm_plan_grid.                 */
+ *   xcd_remap       -1: off, 0: default (on), 1: on. See gemm_plan_grid.
+ *   tail_split      -1: off, 0: default (on), 1: on. With 256x256 tiles, when the last
+ *                   round of the persistent schedule is partial and at most half full
+ *                   (T > P, 0 < T mod P <= P/2), gemm_run stops the persistent launch before
+ *                   those T mod P tiles and enqueues a second launch that computes each of
+ *                   them as four 128x128 quarters (quarters wholly outside the output are
+ *                   skipped). Varlen plans decide on the device, where T is known; their
+ *                   second launch exits at once when there is no such tail. Same results.
+ *                   gemm_run_logged never splits.                                        */
 typedef struct {
   int32_t M, N, K, L;
   int32_t a, b, c, d, post;                              /* gemm_dtype */
@@ -116,6 +124,7 @@ typedef struct {
   int32_t group_m;
   int32_t max_ctas;
   int32_t xcd_remap;
+  int32_t tail_split;
 } gemm_desc;
 
 typedef struct gemm_plan gemm_plan;

@@ -190,6 +190,55 @@ def test_varlen_all_groups_empty():
 
 
 # ---------------------------------------------------------------------------------------
+# split tail: a partial last round of 256x256 tiles runs as 128x128 quarters in a second
+# launch; the results must match the oracle and, bit for bit, the unsplit schedule (each
+# output's k-order and epilogue arithmetic are the same in both kernels)
+# ---------------------------------------------------------------------------------------
+
+def _check_split(inp):
+    d, p, plan = run_hip(inp)
+    T, P = plan.grid()[4:6]
+    if T >= 0:  # dense: the plan knows T
+        assert T > P and 0 < T % P <= P // 2, (T, P)
+    pre, post = problem_of(inp).all(*oracle_codes(inp))
+    tol, rms = tol_for(inp)
+    check_close(d, pre, tol, rms, "D")
+    check_close(p, post, tol, rms, "PostAct")
+    d0, p0, _ = run_hip(inp, tail_split=-1)
+    assert np.array_equal(d, d0)
+    assert np.array_equal(p, p0)
+
+
+def test_split_tail_dense():
+    # T = P + P/16 tiles; the last P/16 (the last M-block row, 100 rows, so the lower
+    # quarters lie wholly outside the output) form the tail
+    P = torch.cuda.get_device_properties(0).multi_processor_count
+    if P % 16:
+        pytest.skip(f"{P} CUs: shape below assumes a multiple of 16")
+    tm = P // 16 + 1
+    inp = small(256 * (tm - 1) + 100, 4024, 72, 1, "bf16", c_dt="f32", d_dt="bf16", post_dt="bf16",
+                act="gelu_tanh", alpha=0.5, beta=0.75, seed=40, gen=lambda s, sh, dt: W.normal(s, sh, dt, 0.5))
+    announce(f"split tail dense M={inp.M} N={inp.N} K={inp.K}")
+    _check_split(inp)
+
+
+def test_split_tail_varlen():
+    # groups of 256-row blocks summing to (P + P/16) / 2 blocks with N = 392 (two N-blocks):
+    # T = P + P/16 map tiles; the last group ends 156 rows short of a block
+    P = torch.cuda.get_device_properties(0).multi_processor_count
+    if P % 32:
+        pytest.skip(f"{P} CUs: shape below assumes a multiple of 32")
+    blocks = [30, 0, 17, 1, 40, 16]
+    blocks.append((P + P // 16) // 2 - sum(blocks))
+    assert blocks[-1] > 0
+    sizes = [256 * b - (156 if i % 2 == 0 and b else 0) for i, b in enumerate(blocks)]
+    sizes[-1] = 256 * blocks[-1] - 156
+    inp = varlen_small(sizes, N=392, K=64, seed=41, act="relu_sq")
+    announce(f"split tail varlen sizes={sizes}")
+    _check_split(inp)
+
+
+# ---------------------------------------------------------------------------------------
 # persistent schedule and FastDivmod, bit for bit
 # ---------------------------------------------------------------------------------------
 
