@@ -135,12 +135,19 @@ class Plan:
             self.handle = None
 
     def run(self, A, B, C=None, D=None, PostAct=None, alpha_dev=None, beta_dev=None,
-            cu_seqlens_m=None, stream=None, tile_log=None, max_iters=0):
+            cu_seqlens_m=None, stream=None, tile_log=None, max_iters=0, tile_counters=None):
         """Enqueue on `stream` (default: torch's current stream). alpha_dev / beta_dev:
-        optional fp32 device tensors of one element, read by the kernel."""
+        optional fp32 device tensors of one element, read by the kernel. tile_counters: an
+        int32 device tensor of 8 zeros selects the dynamic schedule (gemm_run_dynamic; the
+        kernel leaves it zero again)."""
         args = [self.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(PostAct), _ptr(alpha_dev),
                 _ptr(beta_dev), _ptr(cu_seqlens_m)]
-        if tile_log is not None:
+        if tile_counters is not None:
+            if tile_counters.dtype != torch.int32 or tile_counters.numel() < 8 or not tile_counters.is_cuda:
+                raise ValueError("tile_counters: int32 device tensor of at least 8 elements")
+            st = self._lib.gemm_run_dynamic(*args, _ptr(tile_counters), _ptr(tile_log), int(max_iters),
+                                            _stream(stream))
+        elif tile_log is not None:
             st = self._lib.gemm_run_logged(*args, _ptr(tile_log), int(max_iters), _stream(stream))
         else:
             st = self._lib.gemm_run(*args, _stream(stream))

@@ -54,6 +54,8 @@ def load():
         lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.gemm_run_logged.restype = ctypes.c_int
         lib.gemm_run_logged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
+        lib.gemm_run_dynamic.restype = ctypes.c_int
+        lib.gemm_run_dynamic.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
         lib.gemm_destroy.restype = ctypes.c_int
         lib.gemm_destroy.argtypes = [vp]
         lib.gemm_plan_grid.restype = ctypes.c_int

@@ -1,7 +1,9 @@
 """Build libgemm_mi355x.so (the C ABI + gfx950 kernels) in-tree with hipcc.
 
 Every unit is compiled for gfx950 only. Packed-fp32 VALU instructions are disabled
-(-packed-fp32-ops) for all device code.
+(-packed-fp32-ops) for all device code. The atomic optimizer is off: it rewrites the
+dynamic schedule's single-lane tile claim into a per-wave form that waits for the result
+right away instead of where it is used.
 """
 import os
 import shutil
@@ -26,6 +28,7 @@ def hipcc() -> str:
 def flags():
     return ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-Wno-unused-command-line-argument"]
 
 

@@ -42,7 +42,7 @@ static hipError_t launch_key(const KernelKey& key, const KParams& k, hipStream_t
 
 static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
                             void* Post, const float* alpha_dev, const float* beta_dev, const int32_t* cu,
-                            int32_t* tile_log, int32_t max_iters, void* stream) {
+                            int32_t* counters, int32_t* tile_log, int32_t max_iters, void* stream) {
   if (!plan) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: NULL plan");
   // nothing to compute: no tiles (dense) or no rows / columns / groups (varlen)
   const bool empty = plan->varlen ? (plan->base.M == 0 || plan->base.N == 0 || plan->L == 0) : plan->T == 0;
@@ -55,6 +55,7 @@ static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B,
   if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D) || !aligned16(Post))
     return fail(GEMM_ERR_ALIGNMENT, "gemm_run: operand pointers must be 16-byte aligned");
   if (tile_log && max_iters <= 0) return fail(GEMM_ERR_INVALID_ARG, "gemm_run_logged: max_iters <= 0");
+  if (((uintptr_t)counters & 3u) != 0) return fail(GEMM_ERR_ALIGNMENT, "gemm_run_dynamic: tile_counters not 4-byte aligned");
 
   KParams k = plan->base;
   k.A = plan->swapped ? B : A;
@@ -65,6 +66,7 @@ static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B,
   k.alpha_ptr = alpha_dev;
   k.beta_ptr = beta_dev;
   k.cu_seqlens = cu;
+  k.tile_counters = counters;
   k.tile_log = tile_log;
   k.tile_log_iters = tile_log ? max_iters : 0;
   int32_t cus = 0;
@@ -96,6 +98,7 @@ static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B,
   if (e == hipSuccess && p_tail > 0) {
     KParams kt = k;
     kt.tail = 2;
+    kt.tile_counters = nullptr;  // the quarter tiles run the static schedule
     kt.P = p_tail;
     KernelKey key = plan->key;
     key.tile = 1;
@@ -128,14 +131,24 @@ extern "C" {
 
 gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D, void* PostAct,
                      const float* alpha_dev, const float* beta_dev, const int32_t* cu_seqlens_m, void* stream) {
-  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, 0, stream);
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, nullptr, 0, stream);
+}
+
+gemm_status gemm_run_dynamic(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
+                             void* PostAct, const float* alpha_dev, const float* beta_dev,
+                             const int32_t* cu_seqlens_m, int32_t* tile_counters, int32_t* tile_log,
+                             int32_t max_iters, void* stream) {
+  if (!tile_counters) return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_dynamic: NULL tile_counters");
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, tile_counters, tile_log,
+                       max_iters, stream);
 }
 
 gemm_status gemm_run_logged(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
                             void* PostAct, const float* alpha_dev, const float* beta_dev,
                             const int32_t* cu_seqlens_m, int32_t* tile_log, int32_t max_iters, void* stream) {
   if (!tile_log) return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_logged: NULL tile_log");
-  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, tile_log, max_iters, stream);
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, tile_log, max_iters,
+                       stream);
 }
 
 gemm_status gemm_fastdivmod_check(uint32_t d_lo, uint32_t d_hi, uint32_t n_count, unsigned long long* bad_dev,

@@ -385,6 +385,7 @@ struct GemmKernel {
   static constexpr int kLdsBytes = 4 * kStageBytes;
   // varlen group table (tile offsets of the groups, scan partials) past the ring
   static constexpr int kVarlenLds = (kMaxVarlenGroups + 1 + kThreads) * 4;
+  static constexpr int kSlotBytes = 16;  // dynamic schedule: next queue position
   static constexpr int kFrags = kMI + kNI;
   static constexpr int kMfmaPerStep = kMI * kNI;
   static constexpr int kRA = reads_per_frag<A_K, kES>(), kRB = reads_per_frag<B_K, kES>();
@@ -440,7 +441,7 @@ struct GemmKernel {
   // item u = quarter (u & 3) of map tile t_lo + (u >> 2); quarter q covers rows
   // (q & 1) * BM and columns (q >> 1) * BN of it, and may lie wholly outside the output).
   static __device__ __forceinline__ TileInfo decode(const KParams& p, int u, const int32_t* gstart, int t_lo) {
-    const bool quarter = p.tail == 2;
+    const bool quarter = BM == 128 && p.tail == 2;  // (split tails run 128x128 kernels)
     const int MT = quarter ? 2 * BM : BM, NT = quarter ? 2 * BN : BN;
     const int t = quarter ? t_lo + (u >> 2) : u;
     TileInfo ti;
@@ -857,8 +858,10 @@ struct GemmKernel {
     // One LDS object: the varlen group table sits past the ring. (With a second LDS array in
     // the kernel the compiler no longer separates fragment reads from pending global -> LDS
     // transfers and waits for all of them before every read.)
-    __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes + (VARLEN ? kVarlenLds : 0)];
+    __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes + kSlotBytes + (VARLEN ? kVarlenLds : 0)];
     GEP_LDS char* smem = (GEP_LDS char*)smem_raw;
+    // the dynamic schedule's next queue position, published by thread 0
+    volatile int32_t* next_slot = (volatile int32_t*)(smem_raw + kLdsBytes);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     if constexpr (NW == 8) {
@@ -872,14 +875,25 @@ struct GemmKernel {
 
     const int P = p.P;
     const int bid = blockIdx.x;
-    const int bb = (p.xcd_remap && (P & 7) == 0) ? (bid & 7) * (P >> 3) + (bid >> 3) : bid;
+    // With the XCD remap, the P workgroups form 8 queues of Q = P/8 (workgroup b in queue
+    // b % 8 at position b / 8), else one queue of P. Position k of queue x is tile
+    // (k / Q) * P + x * Q + k % Q: the static schedule walks k = j, j + Q, j + 2Q, ...; the
+    // dynamic one (tile_counters given) starts at k = j and then takes k = Q + the value of
+    // an atomic counter per queue, so each queue still holds the same tiles (and L2 reuse)
+    // while its workgroups balance among themselves.
+    const bool xq = p.xcd_remap && (P & 7) == 0;
+    const int Q = xq ? (P >> 3) : P;
+    const int qx = xq ? (bid & 7) : 0;
+    const int qj = xq ? (bid >> 3) : bid;
+    const int bb = qx * Q + qj;
+    auto qtile = [&](int k) { return (k / Q) * P + qx * Q + k % Q; };
 
     // ---- varlen: tile offsets of the groups (in map tiles), in LDS
     [[maybe_unused]] int32_t* gstart = nullptr;
-    [[maybe_unused]] const int MT = p.tail == 2 ? 2 * BM : BM;
+    [[maybe_unused]] const int MT = (BM == 128 && p.tail == 2) ? 2 * BM : BM;
     int T = p.T;
     if constexpr (VARLEN) {
-      int32_t* s_start = (int32_t*)(smem_raw + kLdsBytes);
+      int32_t* s_start = (int32_t*)(smem_raw + kLdsBytes + kSlotBytes);
       int32_t* s_part = s_start + kMaxVarlenGroups + 1;
       const int G = p.L;
       constexpr int kPer = (kMaxVarlenGroups + kThreads - 1) / kThreads;
@@ -948,11 +962,21 @@ struct GemmKernel {
       lb.init(wave, lane, p.N - ti.n0, p.ldb * kES, p.K);
       if constexpr (!kDMA) load_all(la, lb, kt_src(p, ti, 0));
     };
+    // dynamic schedule: this queue's counter, and the number of tiles it holds (the fetch
+    // that returns the last value returns the counter to zero for the next launch)
+    int32_t* const ctr = p.tile_counters ? p.tile_counters + qx : nullptr;
+    const int q_tiles = (U / P) * Q + min(max(U % P - qx * Q, 0), Q);
+    int32_t fetched = 0;
+
     if (bb < U) begin_tile(bb);
     int iter = 0;
-    for (int t = bb; t < U; t += P, ++iter) {
+    for (int t = bb; t < U; ++iter) {
+      // claim the tile after this one (its result is first waited for where it is published)
+      if (ctr && tid == 0) fetched = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (ti.m0 >= ti.row_end || ti.n0 >= p.N) {  // a quarter tile wholly outside the output
-        if (t + P < U) begin_tile(t + P);
+        // (split-tail launches only, which are static)
+        t += P;
+        if (t < U) begin_tile(t);
         continue;
       }
       if (p.tile_log && iter < p.tile_log_iters && tid == 0) {
@@ -965,9 +989,9 @@ struct GemmKernel {
 #pragma unroll
         for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
 
+      // the previous tile's epilogue buffers (and the published queue position) are free
+      lds_barrier();
       if (nk > 0) {
-        // the previous tile's epilogue buffers are free
-        lds_barrier();
         if constexpr (kDMA) {
           // k-tiles 0 and 1 -> stages 0 and 1
           dma_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 0), wave);
@@ -991,11 +1015,17 @@ struct GemmKernel {
       // waits for the stores, and their registers would crowd the epilogue.)
       // (global -> LDS transfers of the padding k-tiles past K must land before the ring is
       // reused)
+      if (ctr && tid == 0) {
+        *next_slot = fetched;
+        if (fetched == q_tiles - 1) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       if constexpr (kDMA) dma_barrier();
       else lds_barrier();
+      // (uniform: keeps the tile loop's state in scalar registers)
+      const int tnext = ctr ? qtile(Q + __builtin_amdgcn_readfirstlane(*next_slot)) : t + P;
       epilogue(p, ti, acc, smem + wave * kEpiRegion, lane, wm0, wn0, alpha, beta);
-      const int tnext = t + P;
-      if (tnext < U) begin_tile(tnext);
+      t = tnext;
+      if (t < U) begin_tile(t);
     }
   }
 };

@@ -42,6 +42,7 @@ struct KParams {
   FastDiv fd_mn;    // tm * tn
   FastDiv fd_Gtn;   // G * tn
   FastDiv fd_tail[1 << kMaxGroupLog2];  // index w: divisor w (1 <= w < G); [0] unused
+  int32_t* tile_counters;  // dynamic schedule: 8 queue counters (zero at launch), or NULL
   int32_t* tile_log;
   int32_t tile_log_iters;
 };

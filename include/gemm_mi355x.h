@@ -165,6 +165,26 @@ gemm_status gemm_run_logged(const gemm_plan* plan, const void* A, const void* B,
                             const int32_t* cu_seqlens_m, int32_t* tile_log, int32_t max_iters,
                             void* stream);
 
+/* As gemm_run (or, with tile_log non-NULL, gemm_run_logged), with the dynamic persistent
+ * schedule: the page 5 GEMM's optional tile_count_semaphore, a device counter from which
+ * persistent workgroups claim their next tile. Here the grid keeps the static schedule's
+ * queues (eight, one per group of P/8 workgroups that the XCD remap keeps on one XCD, or
+ * one queue when the remap is off or P is not a multiple of 8): each workgroup starts on
+ * its static first tile and then claims the next unclaimed tile of its own queue, so a
+ * slow or late compute unit takes fewer tiles while each queue keeps the tiles (and L2
+ * reuse) of the static schedule. Results equal gemm_run's bit for bit; only the tile ->
+ * workgroup assignment changes.
+ * tile_counters: device int32[8], all zero before the first call. Every call returns them
+ * to zero before it completes, so calls in sequence on a stream need no reset; calls that
+ * may run at the same time need separate counters. A call that does not complete (a
+ * faulted context) leaves them undefined. The split tail (tail_split) still applies and
+ * its quarter tiles run statically. Returns INVALID_ARG for NULL tile_counters, ALIGNMENT
+ * if they are not 4-byte aligned, otherwise as gemm_run / gemm_run_logged. */
+gemm_status gemm_run_dynamic(const gemm_plan* plan, const void* A, const void* B, const void* C,
+                             void* D, void* PostAct, const float* alpha_dev, const float* beta_dev,
+                             const int32_t* cu_seqlens_m, int32_t* tile_counters, int32_t* tile_log,
+                             int32_t max_iters, void* stream);
+
 /* Release a plan (NULL is accepted). */
 gemm_status gemm_destroy(gemm_plan* plan);
 

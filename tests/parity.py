@@ -32,7 +32,7 @@ out_like = W.out_like
 
 
 def run_hip(inp, d_major_m=False, tile=None, alpha_dev=None, beta_dev=None, tile_log=None,
-            max_iters=0, **tuning):
+            max_iters=0, tile_counters=None, **tuning):
     """Run the HIP path on the GPU; returns (D, PostAct) as CPU float64 arrays (or None)."""
     from gemm_epilogue_persistent_amd import Plan
     A, B = to_dev(inp.A), to_dev(inp.B)
@@ -43,7 +43,8 @@ def run_hip(inp, d_major_m=False, tile=None, alpha_dev=None, beta_dev=None, tile
     if tile is not None:
         tuning["tile"] = tile
     plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu, **tuning)
-    plan.run(A, B, C, D, P, alpha_dev, beta_dev, cu, tile_log=tile_log, max_iters=max_iters)
+    plan.run(A, B, C, D, P, alpha_dev, beta_dev, cu, tile_log=tile_log, max_iters=max_iters,
+             tile_counters=tile_counters)
     torch.cuda.synchronize()
     d = None if D is None else D.double().cpu().numpy()
     p = None if P is None else P.double().cpu().numpy()

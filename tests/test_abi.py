@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"gemm_create", "gemm_run", "gemm_destroy", "gemm_run_logged", "gemm_plan_grid",
+    assert {"gemm_create", "gemm_run", "gemm_destroy", "gemm_run_logged", "gemm_run_dynamic", "gemm_plan_grid",
             "gemm_fastdivmod_params", "gemm_fastdivmod_check", "gemm_status_string",
             "gemm_last_error"} <= names
     for n in names:

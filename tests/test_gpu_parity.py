@@ -288,6 +288,82 @@ def test_tile_schedule_varlen(tile):
         assert (log[b][len(seq):] == -1).all()
 
 
+# dynamic schedule (gemm_run_dynamic): results equal the static schedule's bit for bit;
+# every tile is taken exactly once, each workgroup starts on its static first tile and takes
+# the rest, in increasing order, from its own queue; the counters are zero afterwards
+
+def _dynamic_log_check(log, T, P, xcd, tile_fn):
+    xq = bool(xcd) and P % 8 == 0
+    Q = P // 8 if xq else P
+    seen = []
+    for b in range(P):
+        ts = [int(x[3]) for x in log[b] if x[3] != -1]
+        for x in log[b]:
+            if x[3] != -1:
+                assert tuple(int(v) for v in x[:3]) == tuple(tile_fn(int(x[3]))), (b, x)
+        if ts:
+            assert ts[0] == oracle.wg_tile(b, 0, P, xq), b
+            assert ts == sorted(ts) and len(set(ts)) == len(ts), b
+            qx = b % 8 if xq else 0
+            assert all(qx * Q <= t % P < (qx + 1) * Q for t in ts), b
+        seen += ts
+    assert sorted(seen) == list(range(T))
+
+
+@pytest.mark.parametrize("xcd", [1, 0])
+def test_dynamic_schedule_dense(xcd):
+    inp = small(8192 - 40, 4096 + 200, 24, 1, "bf16", d_dt="bf16", seed=42)
+    announce(f"dynamic dense xcd={xcd} M={inp.M} N={inp.N}")
+    tune = dict(xcd_remap=1 if xcd else -1)
+    d_static, _, plan = run_hip(inp, **tune)
+    _, _, G, _, T, P = plan.grid()
+    tm, tn = -(-inp.M // 256), -(-inp.N // 256)
+    ctr = torch.zeros(8, dtype=torch.int32, device="cuda")
+    log = torch.full((P * T * 4,), -1, dtype=torch.int32, device="cuda")
+    d_dyn, _, _ = run_hip(inp, tile_log=log, max_iters=T, tile_counters=ctr, **tune)
+    assert (ctr.cpu() == 0).all()
+    assert np.array_equal(d_dyn, d_static)
+    _dynamic_log_check(log.view(P, T, 4).cpu().numpy(), T, P, xcd, lambda t: oracle.tile_dense(t, tm, tn, G))
+    # without a log (the split tail applies), three calls in a row on the same counters
+    for _ in range(3):
+        d_dyn, _, _ = run_hip(inp, tile_counters=ctr, **tune)
+        assert np.array_equal(d_dyn, d_static)
+    assert (ctr.cpu() == 0).all()
+    # the static result against the oracle at sampled points
+    pts = sample_points(inp, 2000, 3)
+    pre, _ = problem_of(inp).points(*oracle_codes(inp), pts)
+    tol, rms = tol_for(inp)
+    check_close(gather(d_static, pts, False), pre, tol, rms, "D sampled")
+
+
+def test_dynamic_schedule_varlen():
+    inp = varlen_small([5000, 0, 3000, 129, 700, 9000, 1, 2048], N=1000, K=16, seed=43)
+    announce(f"dynamic varlen M={inp.M} N={inp.N}")
+    cu = inp.cu_seqlens
+    tn = -(-inp.N // 256)
+    T = oracle.tile_count_varlen(cu, 256, 256, inp.N)
+    d_static, p_static, plan = run_hip(inp)
+    P = plan.grid()[5]
+    assert T > P
+    ctr = torch.zeros(8, dtype=torch.int32, device="cuda")
+    log = torch.full((P * T * 4,), -1, dtype=torch.int32, device="cuda")
+    d_dyn, p_dyn, _ = run_hip(inp, tile_log=log, max_iters=T, tile_counters=ctr)
+    assert (ctr.cpu() == 0).all()
+    assert np.array_equal(d_dyn, d_static) and np.array_equal(p_dyn, p_static)
+    G = plan.grid()[2]
+    _dynamic_log_check(log.view(P, T, 4).cpu().numpy(), T, P, 1,
+                       lambda t: oracle.tile_varlen(t, cu, 256, tn, G))
+    for _ in range(2):
+        d_dyn, p_dyn, _ = run_hip(inp, tile_counters=ctr)
+        assert np.array_equal(d_dyn, d_static) and np.array_equal(p_dyn, p_static)
+    assert (ctr.cpu() == 0).all()
+    pts = sample_points(inp, 2000, 4)
+    pre, post = problem_of(inp).points(*oracle_codes(inp), pts)
+    tol, rms = tol_for(inp)
+    check_close(gather(d_static, pts, True), pre, tol, rms, "D sampled")
+    check_close(gather(p_static, pts, True), post, tol, rms, "PostAct sampled")
+
+
 def test_fastdivmod_device_exhaustive_below_2_16():
     from gemm_epilogue_persistent_amd import fastdivmod_check
     bad = torch.zeros(1, dtype=torch.int64, device="cuda")
