@@ -22,7 +22,7 @@ from ._abi import GemmError, DT, ACT, ROW, COL
 _TORCH_DT = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32",
              torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}
 
-__all__ = ["Plan", "gemm", "gemm_create", "gemm_run", "plan_grid", "fastdivmod_params",
+__all__ = ["Plan", "gemm", "gemm_create", "gemm_run", "plan_grid", "configs", "tune", "fastdivmod_params",
            "fastdivmod_check", "probe_mfma", "GemmError", "library_path"]
 
 
@@ -61,7 +61,7 @@ def _bstride(t):
 
 def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none",
              varlen=False, tile=None, group_m=0, max_ctas=0, xcd_remap=0,
-             tail_split=0):
+             tail_split=0, raster_order=0):
     """Build the gemm_desc for these tensors (no GPU work)."""
     d = _abi.GemmDesc()
     if varlen:
@@ -99,6 +99,7 @@ def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none"
     if tile is not None:
         d.tile_m, d.tile_n = tile
     d.group_m, d.max_ctas, d.xcd_remap, d.tail_split = group_m, max_ctas, xcd_remap, tail_split
+    d.raster_order = raster_order
     return d
 
 
@@ -164,6 +165,12 @@ class Plan:
                                             ctypes.byref(T), ctypes.byref(P)))
         return tuple(o.value for o in out) + (T.value, P.value)
 
+    def raster_along_n(self):
+        """True when the plan's tile map rasters along N (gemm_plan_raster)."""
+        v = ctypes.c_int32()
+        _abi.check(self._lib.gemm_plan_raster(self.handle, ctypes.byref(v)))
+        return bool(v.value)
+
 
 def gemm(A, B, D=None, C=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu_seqlens_m=None,
          alpha_dev=None, beta_dev=None, stream=None, **tuning):
@@ -175,6 +182,44 @@ def gemm(A, B, D=None, C=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu
 
 gemm_run = Plan.run
 plan_grid = Plan.grid
+
+
+def configs(varlen=False):
+    """The tuning space on MI355X: the page 6 quack/gemm_config.py space (tile shape, raster
+    order, swizzle size) with this library's tiles (256x256 with one workgroup per CU, 128x128
+    with two), the raster group size G in {1, 2, 4, 8, 16}, the raster order (along N is dense
+    only) and the XCD remap on or off. Every configuration computes the same bits."""
+    out = []
+    for tile in ((256, 256), (128, 128)):
+        for g in (1, 2, 4, 8, 16):
+            for raster in ((1,) if varlen else (1, 2)):
+                for xcd in (1, -1):
+                    out.append(dict(tile=tile, group_m=g, raster_order=raster, xcd_remap=xcd))
+    return out
+
+
+def tune(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu_seqlens_m=None,
+         candidates=None, steps=10, warmup=3):
+    """Time each candidate configuration (default: configs()) on these operands through
+    gemm_run on the current stream and return (fastest tuning dict, [(ms, tuning), ...] sorted).
+    The outputs are overwritten by the runs."""
+    cands = candidates if candidates is not None else configs(cu_seqlens_m is not None)
+    stream = torch.cuda.current_stream()
+    timed = []
+    for tun in cands:
+        p = Plan(A, B, C, D, PostAct, alpha, beta, act, cu_seqlens_m, **tun)
+        for _ in range(warmup):
+            p.run(A, B, C, D, PostAct, None, None, cu_seqlens_m)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            p.run(A, B, C, D, PostAct, None, None, cu_seqlens_m)
+        end.record(stream)
+        end.synchronize()
+        timed.append((start.elapsed_time(end) / steps, tun))
+    timed.sort(key=lambda x: x[0])
+    return timed[0][1], timed
 
 
 def fastdivmod_params(d):

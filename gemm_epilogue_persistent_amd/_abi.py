@@ -27,7 +27,7 @@ class GemmDesc(ctypes.Structure):
         ("act", ctypes.c_int32), ("varlen_m", ctypes.c_int32),
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
         ("group_m", ctypes.c_int32), ("max_ctas", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-        ("tail_split", ctypes.c_int32),
+        ("tail_split", ctypes.c_int32), ("raster_order", ctypes.c_int32),
     ]
 
 
@@ -62,6 +62,8 @@ def load():
         lib.gemm_plan_grid.argtypes = [vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                        ctypes.POINTER(i32), ctypes.POINTER(i32),
                                        ctypes.POINTER(i64), ctypes.POINTER(i32)]
+        lib.gemm_plan_raster.restype = ctypes.c_int
+        lib.gemm_plan_raster.argtypes = [vp, ctypes.POINTER(i32)]
         lib.gemm_fastdivmod_params.restype = ctypes.c_int
         lib.gemm_fastdivmod_params.argtypes = [u32, ctypes.POINTER(u32), ctypes.POINTER(u32)]
         lib.gemm_fastdivmod_check.restype = ctypes.c_int

@@ -317,27 +317,30 @@ __device__ __forceinline__ void dma_barrier() {
 // ------------------------------------------------------------------------------------
 // Tile scheduler: linear tile id -> (m_blk, n_blk) inside one batch / group
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ void raster(const KParams& p, uint32_t r, uint32_t tm, uint32_t& m, uint32_t& n) {
+// Grouped raster over a grid of ta x tb blocks: groups of G blocks along a (the last group
+// holds the ta % G left over), a fastest inside a group, then b. Raster along M: a = m;
+// along N the roles of M and N are exchanged. fd_Gtb divides by G * tb.
+__device__ __forceinline__ void raster(const KParams& p, uint32_t r, uint32_t ta, uint32_t tb, const FastDiv& fd_Gtb,
+                                       uint32_t& a, uint32_t& b) {
   const uint32_t G = 1u << p.log2G;
-  const uint32_t full = (tm >> p.log2G) << p.log2G;
-  const uint32_t tn = (uint32_t)p.tn;
-  if (r < full * tn) {
+  const uint32_t full = (ta >> p.log2G) << p.log2G;
+  if (r < full * tb) {
     uint32_t grp, w;
-    fd_divmod(p.fd_Gtn, r, grp, w);
-    m = (grp << p.log2G) + (w & (G - 1));
-    n = w >> p.log2G;
+    fd_divmod(fd_Gtb, r, grp, w);
+    a = (grp << p.log2G) + (w & (G - 1));
+    b = w >> p.log2G;
   } else {
-    const uint32_t tail = tm - full;  // 1 <= tail < G
+    const uint32_t tail = ta - full;  // 1 <= tail < G
     // select the constants with static indices (a dynamic index would spill the kernel
     // argument block to scratch)
     FastDiv f = p.fd_tail[1];
 #pragma unroll
     for (int w = 2; w < (1 << kMaxGroupLog2); ++w)
       if (tail == (uint32_t)w) f = p.fd_tail[w];
-    uint32_t nn, mm;
-    fd_divmod(f, r - full * tn, nn, mm);
-    m = full + mm;
-    n = nn;
+    uint32_t bb, aa;
+    fd_divmod(f, r - full * tb, bb, aa);
+    a = full + aa;
+    b = bb;
   }
 }
 
@@ -457,11 +460,12 @@ struct GemmKernel {
       row_base = p.cu_seqlens[lo];
       ti.row_end = p.cu_seqlens[lo + 1];
       const uint32_t tmg = (uint32_t)((ti.row_end - row_base + MT - 1) / MT);
-      raster(p, (uint32_t)(t - gstart[lo]), tmg, mb, nb);
+      raster(p, (uint32_t)(t - gstart[lo]), tmg, (uint32_t)p.tn, p.fd_Gtn, mb, nb);
     } else {
       uint32_t ll, r;
       fd_divmod(p.fd_mn, (uint32_t)t, ll, r);
-      raster(p, r, (uint32_t)p.tm, mb, nb);
+      if (p.raster_n) raster(p, r, (uint32_t)p.tn, (uint32_t)p.tm, p.fd_Gtm, nb, mb);
+      else raster(p, r, (uint32_t)p.tm, (uint32_t)p.tn, p.fd_Gtn, mb, nb);
       ti.l = (int)ll;
       row_base = 0;
       ti.row_end = p.M;

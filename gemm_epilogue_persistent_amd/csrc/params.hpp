@@ -41,6 +41,8 @@ struct KParams {
   int32_t P_big;    // tail != 0: grid of the first launch (the map's round size)
   FastDiv fd_mn;    // tm * tn
   FastDiv fd_Gtn;   // G * tn
+  FastDiv fd_Gtm;   // G * tm (raster along N)
+  int32_t raster_n; // 1: grouped raster along N (dense only)
   FastDiv fd_tail[1 << kMaxGroupLog2];  // index w: divisor w (1 <= w < G); [0] unused
   int32_t* tile_counters;  // dynamic schedule: 8 queue counters (zero at launch), or NULL
   int32_t* tile_log;

@@ -117,6 +117,9 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   if (d.max_ctas < 0) return fail(GEMM_ERR_INVALID_ARG, "max_ctas < 0");
   if (d.xcd_remap < -1 || d.xcd_remap > 1) return fail(GEMM_ERR_INVALID_ARG, "xcd_remap must be -1, 0 or 1");
   if (d.tail_split < -1 || d.tail_split > 1) return fail(GEMM_ERR_INVALID_ARG, "tail_split must be -1, 0 or 1");
+  if (d.raster_order < 0 || d.raster_order > 2) return fail(GEMM_ERR_INVALID_ARG, "raster_order must be 0, 1 or 2");
+  if (d.raster_order == 2 && d.varlen_m)
+    return fail(GEMM_ERR_UNSUPPORTED, "raster along N is not offered for varlen-M (its M-blocks vary per group)");
   if (d.varlen_m && d.L > kMaxVarlenGroups)
     return fail(GEMM_ERR_UNSUPPORTED, "varlen-M supports at most %d groups", kMaxVarlenGroups);
 
@@ -230,6 +233,10 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   k.log2G = log2G;
   k.tn = (int32_t)tn;
   k.fd_Gtn = make_fastdiv((uint32_t)std::max<int64_t>(1, G * tn));
+  k.fd_Gtm = make_fastdiv((uint32_t)std::max<int64_t>(1, G * tm));
+  // default: along N for a single dense GEMM (measured: +5% on 4096^3 with C, D and GELU
+  // PostAct, neutral at 8192^3), along M for batches (the page's order)
+  k.raster_n = (d.raster_order == 2 || (d.raster_order == 0 && !d.varlen_m && d.L == 1)) ? 1 : 0;
   for (int w = 1; w < (1 << kMaxGroupLog2); ++w) k.fd_tail[w] = make_fastdiv((uint32_t)w);
   k.fd_tail[0] = make_fastdiv(1);
   if (d.varlen_m) {
@@ -292,6 +299,12 @@ gemm_status gemm_plan_grid(const gemm_plan* p, int32_t num_cus, int32_t* tile_m,
   if (xcd_remap) *xcd_remap = p->base.xcd_remap;
   if (tiles) *tiles = p->T;
   if (grid) *grid = gep::grid_size(p, num_cus);
+  return GEMM_OK;
+}
+
+gemm_status gemm_plan_raster(const gemm_plan* p, int32_t* along_n) {
+  if (!p || !along_n) return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_plan_raster: NULL argument");
+  *along_n = p->base.raster_n;
   return GEMM_OK;
 }
 

@@ -110,7 +110,13 @@ typedef enum {
  *                   them as four 128x128 quarters (quarters wholly outside the output are
  *                   skipped). Varlen plans decide on the device, where T is known; their
  *                   second launch exits at once when there is no such tail. Same results.
- *                   gemm_run_logged never splits.                                        */
+ *                   gemm_run_logged never splits.
+ *   raster_order    0: default (along N for dense L == 1, else along M), 1: along M,
+ *                   2: along N (dense only). The grouped
+ *                   raster takes groups of group_m blocks along M, M fastest inside a group
+ *                   (page 5's swizzle); along N the roles of M and N are exchanged (page 6,
+ *                   quack/gemm_config.py, keeps the raster order and the swizzle size in
+ *                   its tuning space).                                                   */
 typedef struct {
   int32_t M, N, K, L;
   int32_t a, b, c, d, post;                              /* gemm_dtype */
@@ -125,6 +131,7 @@ typedef struct {
   int32_t max_ctas;
   int32_t xcd_remap;
   int32_t tail_split;
+  int32_t raster_order;
 } gemm_desc;
 
 typedef struct gemm_plan gemm_plan;
@@ -197,13 +204,18 @@ gemm_status gemm_destroy(gemm_plan* plan);
  * XCD remap and P % 8 == 0, b' = (b % 8) * (P / 8) + b / 8. Tile t maps to (m_blk, n_blk,
  * l) by the grouped raster of page 5 (the removed 0.1.10 "CTA swizzle" in GemmSm90.kernel):
  * l = t / (tm * tn); inside a batch, groups of G M-blocks with M fastest, then N, then the
- * next group; the tm % G leftover M-blocks form a last group of that width. Varlen plans
+ * next group; the tm % G leftover M-blocks form a last group of that width (raster along
+ * M; along N, see raster_order and gemm_plan_raster, M and N swap roles). Varlen plans
  * concatenate the groups' tiles in group order (ceil(M_g / tile_m) * tn tiles each) and use
  * the same raster inside a group. All device divisions use FastDivmod (page 6,
  * quack/fast_math.py). Any output pointer may be NULL. */
 gemm_status gemm_plan_grid(const gemm_plan* plan, int32_t num_cus, int32_t* tile_m,
                            int32_t* tile_n, int32_t* group_m, int32_t* xcd_remap,
                            int64_t* tiles, int32_t* grid);
+
+/* The raster order the plan's tile map uses: *along_n = 1 along N, 0 along M (see
+ * raster_order in gemm_desc). INVALID_ARG for a NULL argument. */
+gemm_status gemm_plan_raster(const gemm_plan* plan, int32_t* along_n);
 
 /* FastDivmod constants the library computes for divisor d (1 <= d < 2^31), as page 6,
  * quack/fast_math.py, FastDivmod.create: p = 31 + ceil(log2 d),

@@ -66,6 +66,8 @@ def _load():
         lib.orc_raster.argtypes = [ctypes.c_int64] * 4 + [i64p, i64p]
         lib.orc_tile_dense.restype = None
         lib.orc_tile_dense.argtypes = [ctypes.c_int64] * 4 + [i64p, i64p, i64p]
+        lib.orc_tile_dense_n.restype = None
+        lib.orc_tile_dense_n.argtypes = [ctypes.c_int64] * 4 + [i64p, i64p, i64p]
         lib.orc_tile_varlen.restype = None
         lib.orc_tile_varlen.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)] + \
             [ctypes.c_int64] * 4 + [i64p, i64p, i64p]
@@ -233,9 +235,10 @@ def raster(r, tm, tn, G):
     return m.value, n.value
 
 
-def tile_dense(t, tm, tn, G):
+def tile_dense(t, tm, tn, G, along_n=False):
     m = ctypes.c_int64(); n = ctypes.c_int64(); l = ctypes.c_int64()
-    _load().orc_tile_dense(t, tm, tn, G, ctypes.byref(m), ctypes.byref(n), ctypes.byref(l))
+    f = _load().orc_tile_dense_n if along_n else _load().orc_tile_dense
+    f(t, tm, tn, G, ctypes.byref(m), ctypes.byref(n), ctypes.byref(l))
     return m.value, n.value, l.value
 
 

@@ -340,6 +340,15 @@ void orc_tile_dense(int64_t t, int64_t tm, int64_t tn, int64_t G, int64_t* m, in
   orc_raster(t % (tm * tn), tm, tn, G, m, n);
 }
 
+/* Dense batched, raster along N: the same grouped raster with the roles of M and N
+ * exchanged (groups of G N-blocks, N fastest inside a group; the order option that page 6's
+ * quack/gemm_config.py keeps in its tuning space next to the swizzle size). */
+void orc_tile_dense_n(int64_t t, int64_t tm, int64_t tn, int64_t G, int64_t* m, int64_t* n,
+                      int64_t* l) {
+  *l = t / (tm * tn);
+  orc_raster(t % (tm * tn), tn, tm, G, n, m);
+}
+
 /* Varlen-M: groups in order, group g owning ceil(M_g/TM) * tn consecutive tile ids; empty
  * groups own none. Returns the group in *l and the block inside the group in *m. */
 void orc_tile_varlen(int64_t t, const int32_t* cu, int64_t ngroups, int64_t TM, int64_t tn,

@@ -97,6 +97,8 @@ def test_create_accepts_valid(lib):
     (dict(xcd_remap=2), _abi.INVALID_ARG),
     (dict(tail_split=2), _abi.INVALID_ARG),
     (dict(tail_split=-2), _abi.INVALID_ARG),
+    (dict(raster_order=3), _abi.INVALID_ARG),
+    (dict(varlen_m=1, L=2, sb=65536, raster_order=2), _abi.UNSUPPORTED),
     (dict(varlen_m=1, L=2000, sb=65536), _abi.UNSUPPORTED),
     (dict(varlen_m=1, L=2, sb=65536, d_major=_abi.COL), _abi.UNSUPPORTED),
     (dict(L=2, sa=65536, sb=65536, sd=65536 + 4), _abi.ALIGNMENT),

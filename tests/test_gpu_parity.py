@@ -248,27 +248,52 @@ def device_schedule(inp, P, max_iters, **tuning):
     return log.view(P, max_iters, 4).cpu().numpy()
 
 
-@pytest.mark.parametrize("M,N,L,G,xcd,tile", [(2560, 2176, 2, 8, 0, (256, 256)),
-                                              (2560, 2176, 1, 4, 1, (128, 128)),
-                                              (1280, 4224, 3, 16, 0, (128, 128)),
-                                              (5000 - 8, 512, 1, 1, 0, (256, 256))])
-def test_tile_schedule_dense(M, N, L, G, xcd, tile):
+@pytest.mark.parametrize("M,N,L,G,xcd,tile,along_n", [(2560, 2176, 2, 8, 0, (256, 256), False),
+                                                      (2560, 2176, 1, 4, 1, (128, 128), False),
+                                                      (1280, 4224, 3, 16, 0, (128, 128), False),
+                                                      (5000 - 8, 512, 1, 1, 0, (256, 256), False),
+                                                      (1280, 4224, 2, 8, 1, (256, 256), True),
+                                                      (2560, 2176 - 64, 1, 4, 0, (128, 128), True)])
+def test_tile_schedule_dense(M, N, L, G, xcd, tile, along_n):
     inp = small(M, N, 16, L, "bf16", d_dt="bf16", seed=14)
     tm, tn = -(-M // tile[0]), -(-N // tile[1])
     T = tm * tn * L
-    plan_args = dict(tile=tile, group_m=G, xcd_remap=1 if xcd else -1)
+    plan_args = dict(tile=tile, group_m=G, xcd_remap=1 if xcd else -1, raster_order=2 if along_n else 1)
     _, _, plan = run_hip(inp, **plan_args)
     _, _, Gp, xr, Tp, P = plan.grid()
     assert (Gp, Tp, xr) == (G, T, 1 if xcd else 0)
     max_iters = -(-T // P) + 1
     log = device_schedule(inp, P, max_iters, **plan_args)
-    want = oracle.tile_schedule(P, T, lambda t: oracle.tile_dense(t, tm, tn, G), bool(xcd))
+    want = oracle.tile_schedule(P, T, lambda t: oracle.tile_dense(t, tm, tn, G, along_n), bool(xcd))
     for b in range(P):
         seq = want[b]
         got = log[b]
         assert [tuple(x[:3]) for x in got[:len(seq)]] == [tuple(s) for s in seq], b
         assert (got[len(seq):] == -1).all()
         assert [x[3] for x in got[:len(seq)]] == [oracle.wg_tile(b, i, P, bool(xcd)) for i in range(len(seq))]
+
+
+def test_raster_along_n_results():
+    # same outputs bit for bit as the M raster (only the tile order changes), and the oracle
+    inp = small(1000, 1304, 136, 2, "bf16", c_dt="bf16", d_dt="bf16", post_dt="bf16", act="silu",
+                beta=0.5, seed=44, gen=lambda s, sh, dt: W.normal(s, sh, dt, 0.5))
+    d_n, p_n, _, _ = compare_full(inp, raster_order=2, group_m=4)
+    d_m, p_m, _ = run_hip(inp, raster_order=1, group_m=4)
+    assert np.array_equal(d_n, d_m) and np.array_equal(p_n, p_m)
+
+
+def test_tune_picks_a_config_with_identical_results():
+    from gemm_epilogue_persistent_amd import configs, tune
+    inp = small(1100, 1200, 64, 1, "f16", d_dt="f16", seed=45)
+    d_ref, _, _ = run_hip(inp)
+    A, B = to_dev(inp.A), to_dev(inp.B)
+    D = out_like(inp, "f16")
+    cands = configs()[::5]
+    best, timed = tune(A, B, D=D, candidates=cands, steps=2, warmup=1)
+    assert best in cands and len(timed) == len(cands)
+    assert all(ms > 0 for ms, _ in timed)
+    d_best, _, _ = run_hip(inp, **best)
+    assert np.array_equal(d_best, d_ref)
 
 
 @pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
@@ -314,7 +339,7 @@ def _dynamic_log_check(log, T, P, xcd, tile_fn):
 def test_dynamic_schedule_dense(xcd):
     inp = small(8192 - 40, 4096 + 200, 24, 1, "bf16", d_dt="bf16", seed=42)
     announce(f"dynamic dense xcd={xcd} M={inp.M} N={inp.N}")
-    tune = dict(xcd_remap=1 if xcd else -1)
+    tune = dict(xcd_remap=1 if xcd else -1, raster_order=1)
     d_static, _, plan = run_hip(inp, **tune)
     _, _, G, _, T, P = plan.grid()
     tm, tn = -(-inp.M // 256), -(-inp.N // 256)

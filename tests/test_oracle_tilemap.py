@@ -35,6 +35,28 @@ def test_golden_dense_raster():
         assert oracle.tile_dense(t + tm * tn, tm, tn, G) == (m, n, 1)
 
 
+def test_golden_dense_raster_along_n():
+    rows = _rows("tilemap_dense_n.txt")
+    assert len(rows) == 16
+    for tm, tn, G, t, m, n in rows:
+        assert oracle.tile_dense(t, tm, tn, G, along_n=True) == (m, n, 0)
+        assert oracle.tile_dense(t + tm * tn, tm, tn, G, along_n=True) == (m, n, 1)
+
+
+def test_raster_along_n_bijection_and_g1():
+    r = np.random.Generator(np.random.PCG64(21))
+    for _ in range(60):
+        tm, tn, L = int(r.integers(1, 12)), int(r.integers(1, 40)), int(r.integers(1, 4))
+        G = int(2 ** r.integers(0, 5))
+        T = tm * tn * L
+        seen = {oracle.tile_dense(t, tm, tn, G, along_n=True) for t in range(T)}
+        assert seen == {(m, n, l) for m in range(tm) for n in range(tn) for l in range(L)}
+        assert len(seen) == T
+    # G == 1 along N: groups of one N-block each, M fastest inside, i.e. M runs fastest
+    assert [oracle.tile_dense(t, 3, 4, 1, along_n=True)[:2] for t in range(12)] == \
+        [(t % 3, t // 3) for t in range(12)]
+
+
 def test_golden_varlen():
     cu = [0, 0, 300, 300, 428]
     for t, m, n, g in _rows("tilemap_varlen.txt"):
