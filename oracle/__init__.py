@@ -32,6 +32,7 @@ class _Problem(ctypes.Structure):
         ("alpha", ctypes.c_double), ("beta", ctypes.c_double),
         ("has_c", ctypes.c_int32), ("act", ctypes.c_int32), ("varlen", ctypes.c_int32),
         ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
+        ("dact", ctypes.c_int32),
     ]
 
 
@@ -51,6 +52,8 @@ def _load():
         lib.orc_encode.argtypes = [ctypes.c_int, ctypes.c_double]
         lib.orc_act.restype = ctypes.c_double
         lib.orc_act.argtypes = [ctypes.c_int, ctypes.c_double]
+        lib.orc_dact.restype = ctypes.c_double
+        lib.orc_dact.argtypes = [ctypes.c_int, ctypes.c_double]
         vp = ctypes.c_void_p
         for name in ("orc_gemm_points", "orc_gemm_rows"):
             f = getattr(lib, name)
@@ -123,6 +126,11 @@ def act(name: str, x: float) -> float:
     return _load().orc_act(ACTS[name], float(x))
 
 
+def dact(name: str, x: float) -> float:
+    """act'(x), the factor the activation-backward epilogue applies to the incoming gradient."""
+    return _load().orc_dact(ACTS[name], float(x))
+
+
 # ---------------------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------------------
@@ -133,8 +141,10 @@ class Problem:
 
     def __init__(self, M, N, K, L, a_dt, b_dt, a_kmajor=True, b_kmajor=True, lda=None, ldb=None,
                  sa=0, sb=0, c_dt="none", c_nmajor=True, ldc=None, sc=0, alpha=1.0, beta=1.0,
-                 act="none", cu_seqlens=None):
+                 act="none", cu_seqlens=None, dact=False):
         self.M, self.N, self.K, self.L = M, N, K, L
+        self.dact = bool(dact)
+        assert not self.dact or c_dt != "none", "the activation-backward epilogue reads C"
         self.a_dt, self.b_dt, self.c_dt = a_dt, b_dt, c_dt
         self.a_kmajor, self.b_kmajor, self.c_nmajor = a_kmajor, b_kmajor, c_nmajor
         self.lda = lda if lda is not None else (K if a_kmajor else M)
@@ -155,6 +165,7 @@ class Problem:
         s.has_c = int(self.c_dt != "none")
         s.act = ACTS[self.act]
         s.varlen = int(self.cu_seqlens is not None)
+        s.dact = int(self.dact)
         if self.cu_seqlens is not None:
             assert len(self.cu_seqlens) == self.L + 1
             s.cu_seqlens = self.cu_seqlens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
@@ -222,7 +233,8 @@ def problem_from(inp, act=None, alpha=None, beta=None):
                    lda=lda, ldb=ldb, sa=sa, sb=B.stride(0),
                    alpha=inp.alpha if alpha is None else alpha,
                    beta=inp.beta if beta is None else beta,
-                   act=inp.act if act is None else act, cu_seqlens=inp.cu_seqlens, **kw)
+                   act=inp.act if act is None else act, cu_seqlens=inp.cu_seqlens,
+                   dact=getattr(inp, "dact", False), **kw)
 
 
 # ---------------------------------------------------------------------------------------

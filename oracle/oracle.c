@@ -146,6 +146,34 @@ double orc_act(int act, double x) {
   }
 }
 
+/* Derivative act'(x) of each activation above, in fp64, for the activation-backward
+ * epilogue (page 6, quack/gemm_dact_sm90.py: dact_fn_map maps relu, relu_sq and
+ * gelu_tanh_approx to functions of (x, dout) returning (dx, act(x)); their bodies are not on
+ * the pages). Written from the formulas above by the product and chain rules:
+ *   relu:     1 for x > 0, else 0 (the derivative at 0 taken as 0)
+ *   relu_sq:  2 max(x, 0)
+ *   gelu:     with c = sqrt(2/pi), u = c (x + 0.044715 x^3), t = tanh(u):
+ *             (1 + t)/2 + x/2 (1 - t^2) c (1 + 3 * 0.044715 x^2)
+ *   silu:     with s = 1/(1 + e^-x): s + x s (1 - s)        (an addition: not on the pages)
+ *   none:     1 */
+double orc_dact(int act, double x) {
+  switch (act) {
+    case ORC_ACT_NONE: return 1.0;
+    case ORC_ACT_RELU: return x > 0.0 ? 1.0 : 0.0;
+    case ORC_ACT_RELU_SQ: return x > 0.0 ? 2.0 * x : 0.0;
+    case ORC_ACT_GELU_TANH: {
+      double c = sqrt(2.0 / M_PI);
+      double t = tanh(c * (x + 0.044715 * x * x * x));
+      return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x);
+    }
+    case ORC_ACT_SILU: {
+      double sg = 1.0 / (1.0 + exp(-x));
+      return sg + x * sg * (1.0 - sg);
+    }
+    default: return NAN;
+  }
+}
+
 /* ------------------------------------------------------------------------------------ */
 /* The GEMM problem.                                                                    */
 /* ------------------------------------------------------------------------------------ */
@@ -169,6 +197,7 @@ typedef struct {
   int32_t act;
   int32_t varlen;
   const int32_t* cu_seqlens; /* host array, L+1 entries, when varlen */
+  int32_t dact;              /* 1: activation-backward epilogue, C holds the pre-activation */
 } orc_problem;
 
 static double load_elem(const void* base, int dt, int64_t idx) {
@@ -189,7 +218,11 @@ static int64_t group_of_row(const orc_problem* p, int64_t r) {
   return -1;
 }
 
-/* One output element: pre = alpha * sum_k A*B + beta * C, post = act(pre). */
+/* One output element: pre = alpha * sum_k A*B + beta * C, post = act(pre).
+ * Activation-backward (dact, page 6 GemmDActSm90.epi_visit_acc_subtile): the GEMM gives the
+ * incoming gradient dout = alpha * sum_k A*B (alpha = 1 on the page, which has none), C is
+ * the saved pre-activation x; then pre (the D output) = dout * act'(x) and post (PostAct) =
+ * act(x); with no activation D = dout and PostAct = x. beta is not used. */
 static void elem(const orc_problem* p, const void* A, const void* B, const void* C, int64_t l,
                  int64_t m, int64_t n, double* pre, double* post) {
   int64_t lb = l;   /* batch index used for B */
@@ -205,6 +238,13 @@ static void elem(const orc_problem* p, const void* A, const void* B, const void*
     acc += load_elem(A, p->a_dt, ia) * load_elem(B, p->b_dt, ib);
   }
   double v = p->alpha * acc;
+  if (p->dact) {
+    int64_t ic = lx * p->sc + (p->c_nmajor ? m * p->ldc + n : n * p->ldc + m);
+    double x = load_elem(C, p->c_dt, ic);
+    *pre = v * orc_dact(p->act, x);
+    *post = orc_act(p->act, x);
+    return;
+  }
   if (p->has_c) {
     int64_t ic = lx * p->sc + (p->c_nmajor ? m * p->ldc + n : n * p->ldc + m);
     v += p->beta * load_elem(C, p->c_dt, ic);

@@ -44,6 +44,7 @@ class Inputs:
     beta: float = 1.0
     act: str = "none"
     cu_seqlens: Optional[np.ndarray] = None
+    dact: bool = False  # activation backward: C is the pre-activation, D = (alpha A x B) * act'(C)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -182,6 +183,20 @@ def fp8_8192():
                   alpha=alpha, extra={"scale_a": sa, "scale_b": sb})
 
 
+def dact_4096(act="gelu_tanh"):
+    """Activation backward at 4096^3 bf16 (page 6, gemm_dact_sm90): A = the incoming gradient
+    and B = the weight, both ~ N(0,1)/sqrt(K); C = the saved pre-activation ~ N(0,1) (the
+    forward workload's scale); D = dout * act'(C) and PostAct = act(C), bf16."""
+    s = 1111 + 10 * 5
+    M = N = K = 4096
+    std = 1.0 / np.sqrt(K)
+    A = normal(s + 0, (1, M, K), "bf16", std)
+    B = normal(s + 1, (1, N, K), "bf16", std)
+    C = normal(s + 2, (1, M, N), "bf16")
+    return Inputs(f"dact_4096_bf16_{act}", M, N, K, 1, "bf16", "bf16", A, B, C=C, c_dt="bf16",
+                  d_dt="bf16", post_dt="bf16", act=act, dact=True)
+
+
 def group_sizes(seed, G, unit=128, max_units=32):
     return rng(seed).integers(1, max_units + 1, size=G) * unit
 
@@ -210,6 +225,7 @@ WORKLOADS = {
     "batched_2048": batched_2048,
     "fp8_8192": fp8_8192,
     "varlen_moe": varlen_moe,
+    "dact_4096": dact_4096,
 }
 
 
