@@ -23,7 +23,7 @@ METRIC = "GEMM TFLOPS and % of MFMA peak at 8192^3 bf16/fp8; varlen-M grouped TF
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "e5m2": 5000.0}
 HBM_PEAK_GBS = 8000.0
 PRIMARY = "square_8192_bf16"
-SECONDARY = ["fp8_8192", "varlen_moe", "square_8192_f16", "act_4096", "batched_2048"]
+SECONDARY = ["fp8_8192", "varlen_moe", "square_8192_f16", "act_4096", "batched_2048", "dact_4096"]
 
 
 def source_hash():
@@ -60,6 +60,8 @@ def setup(name, **tuning):
     D = out_like(inp, inp.d_dt) if inp.d_dt != "none" else None
     P = out_like(inp, inp.post_dt) if inp.post_dt != "none" else None
     cu = torch.from_numpy(inp.cu_seqlens).to("cuda") if inp.varlen else None
+    if inp.dact:
+        tuning = dict(tuning, dact=True)
     plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu, **tuning)
     args = (A, B, C, D, P, None, None, cu)
     return inp, plan, args

@@ -22,7 +22,7 @@ from ._abi import GemmError, DT, ACT, ROW, COL
 _TORCH_DT = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32",
              torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}
 
-__all__ = ["Plan", "gemm", "gemm_create", "gemm_run", "plan_grid", "configs", "tune", "fastdivmod_params",
+__all__ = ["Plan", "gemm", "gemm_dact", "gemm_create", "gemm_run", "plan_grid", "configs", "tune", "fastdivmod_params",
            "fastdivmod_check", "probe_mfma", "GemmError", "library_path"]
 
 
@@ -61,7 +61,7 @@ def _bstride(t):
 
 def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none",
              varlen=False, tile=None, group_m=0, max_ctas=0, xcd_remap=0,
-             tail_split=0, raster_order=0):
+             tail_split=0, raster_order=0, dact=False):
     """Build the gemm_desc for these tensors (no GPU work)."""
     d = _abi.GemmDesc()
     if varlen:
@@ -100,6 +100,7 @@ def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none"
         d.tile_m, d.tile_n = tile
     d.group_m, d.max_ctas, d.xcd_remap, d.tail_split = group_m, max_ctas, xcd_remap, tail_split
     d.raster_order = raster_order
+    d.dact = 1 if dact else 0
     return d
 
 
@@ -178,6 +179,15 @@ def gemm(A, B, D=None, C=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu
     p = Plan(A, B, C, D, PostAct, alpha, beta, act, cu_seqlens_m, **tuning)
     p.run(A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, stream)
     return D if D is not None else PostAct
+
+
+def gemm_dact(A, B, PreAct, D, PostAct=None, act="none", alpha=1.0, cu_seqlens_m=None, alpha_dev=None,
+              stream=None, **tuning):
+    """Activation backward (page 6, gemm_dact_sm90): D = (alpha * A x B) * act'(PreAct) and,
+    if given, PostAct = act(PreAct). Outputs are written in place; returns D."""
+    p = Plan(A, B, PreAct, D, PostAct, alpha, 1.0, act, cu_seqlens_m, dact=True, **tuning)
+    p.run(A, B, PreAct, D, PostAct, alpha_dev, None, cu_seqlens_m, stream)
+    return D
 
 
 gemm_run = Plan.run

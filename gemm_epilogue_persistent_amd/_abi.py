@@ -27,7 +27,7 @@ class GemmDesc(ctypes.Structure):
         ("act", ctypes.c_int32), ("varlen_m", ctypes.c_int32),
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
         ("group_m", ctypes.c_int32), ("max_ctas", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-        ("tail_split", ctypes.c_int32), ("raster_order", ctypes.c_int32),
+        ("tail_split", ctypes.c_int32), ("raster_order", ctypes.c_int32), ("dact", ctypes.c_int32),
     ]
 
 

@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm_mi355x.so")
-UNITS = ["plan.cpp", "gemm_api.hip", "inst_f16.hip", "inst_bf16.hip", "inst_fp8.hip", "probe.hip"]
+UNITS = ["plan.cpp", "gemm_api.hip", "inst_f16.hip", "inst_bf16.hip", "inst_fp8.hip", "inst_f16_dact.hip",
+         "inst_bf16_dact.hip", "inst_fp8_dact.hip", "probe.hip"]
 
 
 def hipcc() -> str:

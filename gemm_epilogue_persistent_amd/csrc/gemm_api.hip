@@ -33,10 +33,11 @@ static gemm_status current_cus(int32_t* cus) {
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static hipError_t launch_key(const KernelKey& key, const KParams& k, hipStream_t s) {
+  const bool da = key.dact != 0;
   switch (key.op) {
-    case OP_F16: return launch_f16(key, k, s);
-    case OP_BF16: return launch_bf16(key, k, s);
-    default: return launch_fp8(key, k, s);
+    case OP_F16: return da ? launch_family<OP_F16, true>(key, k, s) : launch_family<OP_F16, false>(key, k, s);
+    case OP_BF16: return da ? launch_family<OP_BF16, true>(key, k, s) : launch_family<OP_BF16, false>(key, k, s);
+    default: return da ? launch_family<OP_FP8, true>(key, k, s) : launch_family<OP_FP8, false>(key, k, s);
   }
 }
 
@@ -52,6 +53,7 @@ static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B,
   if (plan->has_d != (D != nullptr)) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: D must be given iff the plan has a D type");
   if (plan->has_p != (Post != nullptr)) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: PostAct must be given iff the plan has a PostAct type");
   if (plan->varlen && !cu) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: cu_seqlens_m is required for a varlen plan");
+  if (plan->key.dact && beta_dev) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: a dact plan takes no beta");
   if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D) || !aligned16(Post))
     return fail(GEMM_ERR_ALIGNMENT, "gemm_run: operand pointers must be 16-byte aligned");
   if (tile_log && max_iters <= 0) return fail(GEMM_ERR_INVALID_ARG, "gemm_run_logged: max_iters <= 0");

@@ -269,6 +269,29 @@ __device__ __forceinline__ float act_fn(float x) {
   }
 }
 
+// act'(x) for the activation-backward epilogue (page 6, quack/gemm_dact_sm90.py: dact_fn_map
+// pairs each activation with a function of (x, dout) returning (dout * act'(x), act(x)); the
+// derivative bodies are not on the pages and follow from the forms above): relu: [x > 0];
+// relu_sq: 2 max(x, 0); GELU-tanh x * s with s = sigmoid(2u): s + x s (1 - s) * 2u', where
+// 2u' = 2 sqrt(2/pi) (1 + 3 * 0.044715 x^2); SiLU (added here): s + x s (1 - s), s = sigmoid(x).
+template <int ACT>
+__device__ __forceinline__ float dact_fn(float x) {
+  if constexpr (ACT == ACT_RELU) {
+    return x > 0.f ? 1.f : 0.f;
+  } else if constexpr (ACT == ACT_RELU_SQ) {
+    return x > 0.f ? 2.f * x : 0.f;
+  } else if constexpr (ACT == ACT_GELU_TANH) {
+    const float x2 = x * x;
+    const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp(-1.5957691216057308f * (x + 0.044715f * x2 * x)));
+    return sg + x * sg * (1.f - sg) * (1.5957691216057308f * (1.f + 0.134145f * x2));
+  } else if constexpr (ACT == ACT_SILU) {
+    const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp(-x));
+    return sg + x * sg * (1.f - sg);
+  } else {
+    return 1.f;
+  }
+}
+
 // Four fp32 values as the 8 bytes of 4 bf16 / f16 (round to nearest even).
 __device__ __forceinline__ uint2 pack4_16(int dt, const float v[4]) {
   uint2 x;
@@ -354,7 +377,7 @@ struct TileInfo {
 };
 
 
-template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, bool VARLEN, int NW>
+template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, bool VARLEN, int NW, bool DACT = false>
 struct GemmKernel {
   // NW wave64s in a 2 x (NW/2) grid over the output tile
   static constexpr int kThreads = NW * 64;
@@ -716,6 +739,31 @@ struct GemmKernel {
     return w;
   }
 
+  static __device__ __forceinline__ f32x8 dact8(int act, const f32x8& v) {
+    f32x8 w;
+    switch (act) {
+      case ACT_RELU:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = dact_fn<ACT_RELU>(v[e]);
+        break;
+      case ACT_RELU_SQ:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = dact_fn<ACT_RELU_SQ>(v[e]);
+        break;
+      case ACT_GELU_TANH:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = dact_fn<ACT_GELU_TANH>(v[e]);
+        break;
+      case ACT_SILU:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = dact_fn<ACT_SILU>(v[e]);
+        break;
+      default:
+        w = f32x8{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+    }
+    return w;
+  }
+
   // Everything a pass needs about the wave's part of the output tile.
   struct EpiArgs {
     const char* cb;  // C, D, PostAct at the wave tile's first row and column
@@ -729,7 +777,8 @@ struct GemmKernel {
   // Without C the pass issues no global load, so no wait in it covers its own stores (a
   // wait on a load after a store is a vmcnt(0): loads and stores share the counter); with
   // C the loads of a batch of kCB row groups are issued together, one wait per batch.
-  template <int DT, bool HC>
+  // BWD (activation backward; C present): D = (alpha * acc) * act'(C), PostAct = act(C).
+  template <int DT, bool HC, bool BWD = false>
   static __device__ __forceinline__ void pass_fast(const KParams& p, const EpiArgs& ea, const GEP_LDS char* buf,
                                                    int m0, int lane) {
     constexpr int kCB = kIt < 4 ? kIt : 4;  // row groups per batch
@@ -753,6 +802,17 @@ struct GemmKernel {
         const f32x4 x0 = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, 0));
         const f32x4 x1 = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, 1));
         f32x8 v = f32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]} * ea.alpha;
+        if constexpr (BWD) {
+          const f32x8 pre = unpack8<DT>(cv[u]);
+          if (col_ok && m < ea.rows_valid) {
+            if (hd) *(i32x4*)(ea.db + ((int64_t)m * p.ldd + 8 * c8) * 2) = pack8<DT>(v * dact8(p.act, pre));
+            if (hp) *(i32x4*)(ea.pb + ((int64_t)m * p.ldp + 8 * c8) * 2) = pack8<DT>(act8(p.act, pre));
+          }
+          // one row group at a time: interleaved, their temporaries would crowd out the
+          // registers the main loop keeps
+          __builtin_amdgcn_sched_barrier(0);
+          continue;
+        }
         if constexpr (HC) v += ea.beta * unpack8<DT>(cv[u]);
         if (col_ok && m < ea.rows_valid) {
           if (hd) *(i32x4*)(ea.db + ((int64_t)m * p.ldd + 8 * c8) * 2) = pack8<DT>(v);
@@ -766,16 +826,30 @@ struct GemmKernel {
   static __device__ __forceinline__ void finish4(const KParams& p, const char* cp, char* dp, char* pp,
                                                  const f32x4& x, float alpha, float beta) {
     float v[4] = {x[0] * alpha, x[1] * alpha, x[2] * alpha, x[3] * alpha};
+    float c[4] = {0.f, 0.f, 0.f, 0.f};
     if (p.c_dt != DT_NONE) {
-      float c[4];
       if (p.c_dt == DT_F32) {
         const f32x4 y = *(const f32x4*)cp;
         c[0] = y[0]; c[1] = y[1]; c[2] = y[2]; c[3] = y[3];
       } else {
         unpack4_16(p.c_dt, *(const uint2*)cp, c);
       }
+      if constexpr (!DACT) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
+      }
+    }
+    if constexpr (DACT) {
+      // activation backward: D = dout * act'(C), PostAct = act(C)
+      const f32x8 c8 = f32x8{c[0], c[1], c[2], c[3], 0.f, 0.f, 0.f, 0.f};
+      const f32x8 g = dact8(p.act, c8), w8 = act8(p.act, c8);
+      float d[4] = {v[0] * g[0], v[1] * g[1], v[2] * g[2], v[3] * g[3]};
+      float w[4] = {w8[0], w8[1], w8[2], w8[3]};
+      if (p.d_dt == DT_F32) *(f32x4*)dp = f32x4{d[0], d[1], d[2], d[3]};
+      else if (p.d_dt != DT_NONE) *(uint2*)dp = pack4_16(p.d_dt, d);
+      if (p.p_dt == DT_F32) *(f32x4*)pp = f32x4{w[0], w[1], w[2], w[3]};
+      else if (p.p_dt != DT_NONE) *(uint2*)pp = pack4_16(p.p_dt, w);
+      return;
     }
     if (p.d_dt == DT_F32) *(f32x4*)dp = f32x4{v[0], v[1], v[2], v[3]};
     else if (p.d_dt != DT_NONE) *(uint2*)dp = pack4_16(p.d_dt, v);
@@ -846,7 +920,12 @@ struct GemmKernel {
       // LDS operations of one wave complete in order; keep the compiler from reordering
       asm volatile("" ::: "memory");
       const int m0 = pass * kBPP * 32;
-      if (path == 1) {
+      if constexpr (DACT) {
+        // (C is always present)
+        if (path == 1) pass_fast<DT_BF16, true, true>(p, ea, region, m0, lane);
+        else if (path == 2) pass_fast<DT_F16, true, true>(p, ea, region, m0, lane);
+        else pass_generic(p, ea, region, m0, lane);
+      } else if (path == 1) {
         if (p.c_dt != DT_NONE) pass_fast<DT_BF16, true>(p, ea, region, m0, lane);
         else pass_fast<DT_BF16, false>(p, ea, region, m0, lane);
       } else if (path == 2) {

@@ -60,6 +60,7 @@ struct KernelKey {
   int32_t b_kmajor;
   int32_t tile;      // 0: 256x256, 1: 128x128
   int32_t varlen;
+  int32_t dact;      // activation-backward epilogue
 };
 
 }  // namespace gep

@@ -96,8 +96,16 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
     if (!is_output_type(outs[i])) return fail(GEMM_ERR_UNSUPPORTED, "C/D/PostAct must be f16, bf16 or f32");
   }
   if (d.d == DT_NONE && d.post == DT_NONE) return fail(GEMM_ERR_INVALID_ARG, "neither D nor PostAct requested");
-  if (d.act != GEMM_ACT_NONE && d.post == DT_NONE)
+  if (d.dact != 0 && d.dact != 1) return fail(GEMM_ERR_INVALID_ARG, "dact must be 0 or 1");
+  if (d.dact) {
+    // activation backward (page 6, gemm_dact_sm90): C is the saved pre-activation, D the
+    // gradient dout * act'(C); beta has no role there
+    if (d.c == DT_NONE) return fail(GEMM_ERR_INVALID_ARG, "dact: C (the pre-activation) is required");
+    if (d.d == DT_NONE) return fail(GEMM_ERR_INVALID_ARG, "dact: D (the gradient) is required");
+    if (d.beta != 1.0f) return fail(GEMM_ERR_INVALID_ARG, "dact: beta is not used and must be 1");
+  } else if (d.act != GEMM_ACT_NONE && d.post == DT_NONE) {
     return fail(GEMM_ERR_INVALID_ARG, "an activation needs a PostAct output");
+  }
 
   // ---- output majors
   int32_t out_major = -1;
@@ -201,6 +209,7 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   key.a_kmajor = amaj == GEMM_ROW ? 1 : 0;
   key.b_kmajor = bmaj == GEMM_ROW ? 1 : 0;
   key.varlen = d.varlen_m;
+  key.dact = d.dact;
 
   // ---- tile choice
   int32_t tmn = 0;

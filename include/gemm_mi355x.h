@@ -93,6 +93,14 @@ typedef enum {
  * C, D and PostAct that are present must share one major mode.
  * Varlen mode supports only GEMM_ROW outputs.
  *
+ * Activation backward (dact = 1; page 6, quack/gemm_dact_sm90.py, GemmDActSm90): the product
+ * is the incoming gradient dout = alpha * A x B, C holds the saved pre-activation x (its
+ * own type), and the outputs are D = dout * act'(x) (required) and PostAct = act(x)
+ * (optional); with act NONE, D = dout and PostAct = x. act'(x): relu [x > 0], relu_sq
+ * 2 max(x, 0), gelu_tanh the derivative of the tanh form above, silu s (1 + x (1 - s)) with
+ * s = 1 / (1 + exp(-x)) (silu is an addition: the page maps relu, relu_sq and gelu only).
+ * beta has no role: it must be 1 and gemm_run takes no beta_dev. C is required.
+ *
  * Alignment (page 5, constraints of the dense GEMM docstring): the contiguous dimension
  * of every operand must hold a whole number of 16-byte chunks (a multiple of 8 elements
  * for 16-bit types, 16 for fp8, 4 for f32), and every leading-dimension and batch stride
@@ -132,6 +140,7 @@ typedef struct {
   int32_t xcd_remap;
   int32_t tail_split;
   int32_t raster_order;
+  int32_t dact;     /* 1: activation-backward epilogue (see above) */
 } gemm_desc;
 
 typedef struct gemm_plan gemm_plan;

@@ -42,6 +42,8 @@ def run_hip(inp, d_major_m=False, tile=None, alpha_dev=None, beta_dev=None, tile
     cu = torch.from_numpy(inp.cu_seqlens).to("cuda") if inp.varlen else None
     if tile is not None:
         tuning["tile"] = tile
+    if inp.dact:
+        tuning["dact"] = True
     plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu, **tuning)
     plan.run(A, B, C, D, P, alpha_dev, beta_dev, cu, tile_log=tile_log, max_iters=max_iters,
              tile_counters=tile_counters)

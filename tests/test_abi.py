@@ -98,6 +98,9 @@ def test_create_accepts_valid(lib):
     (dict(tail_split=2), _abi.INVALID_ARG),
     (dict(tail_split=-2), _abi.INVALID_ARG),
     (dict(raster_order=3), _abi.INVALID_ARG),
+    (dict(dact=1), _abi.INVALID_ARG),  # dact without C
+    (dict(dact=1, c=2, ldc=256, beta=0.5), _abi.INVALID_ARG),  # dact takes no beta
+    (dict(dact=2, c=2, ldc=256), _abi.INVALID_ARG),
     (dict(varlen_m=1, L=2, sb=65536, raster_order=2), _abi.UNSUPPORTED),
     (dict(varlen_m=1, L=2000, sb=65536), _abi.UNSUPPORTED),
     (dict(varlen_m=1, L=2, sb=65536, d_major=_abi.COL), _abi.UNSUPPORTED),

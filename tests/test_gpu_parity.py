@@ -147,6 +147,63 @@ def test_identity_exact():
 
 
 # ---------------------------------------------------------------------------------------
+# activation backward (dact): D = (alpha A x B) * act'(C), PostAct = act(C)
+# ---------------------------------------------------------------------------------------
+
+def small_dact(M, N, K, L, act, c_dt="bf16", d_dt="bf16", post_dt="bf16", alpha=1.0, seed=50):
+    inp = small(M, N, K, L, "bf16", c_dt=c_dt, d_dt=d_dt, post_dt=post_dt, act=act, alpha=alpha,
+                seed=seed, gen=lambda s, sh, dt: W.normal(s, sh, dt, 0.5))
+    inp.C = W.normal(700 + seed, (L, M, N), c_dt, 1.5) if c_dt != "none" else None
+    inp.dact = True
+    return inp
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+@pytest.mark.parametrize("act", ["none", "relu", "relu_sq", "gelu_tanh", "silu"])
+def test_small_dact(tile, act):
+    compare_full(small_dact(296, 392, 136, 1, act, alpha=0.75), tile=tile)
+
+
+@pytest.mark.parametrize("c_dt,d_dt,post_dt", [("f32", "f16", "f32"), ("f16", "f16", "none"),
+                                               ("bf16", "f32", "bf16")])
+def test_small_dact_types_and_batches(c_dt, d_dt, post_dt):
+    compare_full(small_dact(200, 264, 72, 2, "gelu_tanh", c_dt=c_dt, d_dt=d_dt, post_dt=post_dt, seed=51))
+
+
+def test_dact_small_integers_exact():
+    r = np.random.Generator(np.random.PCG64(52))
+    M, N, K = 136, 200, 96
+    a = r.integers(-3, 4, size=(1, M, K)).astype(np.float64)
+    b = r.integers(-3, 4, size=(1, N, K)).astype(np.float64)
+    c = r.integers(-6, 7, size=(1, M, N)).astype(np.float64) / 2.0
+    for act in ("none", "relu", "relu_sq"):
+        inp = W.Inputs("dact_ints", M, N, K, 1, "bf16", "bf16", W.to_dtype(a, "bf16"), W.to_dtype(b, "bf16"),
+                       C=W.to_dtype(c, "bf16"), c_dt="bf16", d_dt="f32", post_dt="f32", act=act, dact=True)
+        d, p, _ = run_hip(inp)
+        pre, post = problem_of(inp).all(*oracle_codes(inp))
+        assert np.array_equal(d, pre) and np.array_equal(p, post), act
+
+
+def test_dact_varlen_and_device_alpha():
+    inp = varlen_small([0, 300, 129, 0, 255], K=72, act="gelu_tanh", seed=53)
+    inp.C = W.normal(1053, (inp.M, inp.N), "bf16", 1.5)
+    inp.c_dt = "bf16"
+    inp.beta = 1.0
+    inp.dact = True
+    compare_full(inp)
+    a = torch.tensor([-0.5], dtype=torch.float32, device="cuda")
+    d, p, _ = run_hip(inp, alpha_dev=a)
+    pre, post = problem_of(inp, alpha=-0.5).all(*oracle_codes(inp))
+    tol, rms = tol_for(inp)
+    check_close(d, pre, tol, rms, "D")
+    check_close(p, post, tol, rms, "PostAct")
+
+
+def test_workload_dact_4096():
+    full_size(W.dact_4096())
+
+
+# ---------------------------------------------------------------------------------------
 # varlen-M
 # ---------------------------------------------------------------------------------------
 
