@@ -113,8 +113,41 @@ static uint32_t encode_binary16like(double x, int ebits, int mbits) {
   return (sign << (ebits + mbits)) | (efield << mbits) | mfield;
 }
 
+/* OCP fp8 with round-to-nearest-even and saturation to the largest finite value
+ * ("satfinite": what a D / PostAct output in an fp8 type receives; page 5's is_valid_dtypes
+ * admits Float8E4M3FN and Float8E5M2 for D). Magnitudes above the largest finite value,
+ * infinities included, become it; NaN stays NaN (e4m3fn: S.1111.111; e5m2: S.11111.10).
+ * e4m3fn has no infinity, so its top exponent holds normal numbers up to 448. */
+static uint32_t encode_fp8_satfinite(double x, int ebits, int mbits) {
+  int fn = ebits == 4; /* e4m3fn */
+  int bias = (1 << (ebits - 1)) - 1;
+  int emin = 1 - bias;
+  uint32_t sign = signbit(x) ? 1u : 0u;
+  uint32_t top = (1u << ebits) - 1u;
+  if (isnan(x)) return (sign << 7) | (fn ? 0x7Fu : ((top << mbits) | (1u << (mbits - 1))));
+  double maxfin = fn ? 448.0 : 57344.0;
+  double a = fabs(x);
+  double r = isinf(a) ? maxfin : (a == 0.0 ? 0.0 : round_to_format(a, mbits, emin));
+  if (r > maxfin) r = maxfin;
+  if (r == 0.0) return sign << 7;
+  int e;
+  frexp(r, &e);
+  int ex = e - 1;
+  uint32_t efield, mfield;
+  if (ex < emin) {
+    efield = 0;
+    mfield = (uint32_t)ldexp(r, -(emin - mbits));
+  } else {
+    efield = (uint32_t)(ex + bias);
+    mfield = (uint32_t)(ldexp(r, -(ex - mbits)) - ldexp(1.0, mbits));
+  }
+  return (sign << 7) | (efield << mbits) | mfield;
+}
+
 uint32_t orc_encode(int dt, double x) {
   switch (dt) {
+    case ORC_E4M3: return encode_fp8_satfinite(x, 4, 3);
+    case ORC_E5M2: return encode_fp8_satfinite(x, 5, 2);
     case ORC_F16: return encode_binary16like(x, 5, 10);
     case ORC_BF16: return encode_binary16like(x, 8, 7);
     case ORC_F32: {
@@ -346,6 +379,7 @@ void orc_encode_array(int dt, int64_t n, const double* x, void* out) {
   for (int64_t i = 0; i < n; ++i) {
     uint32_t c = orc_encode(dt, x[i]);
     if (dt == ORC_F32) ((uint32_t*)out)[i] = c;
+    else if (dt == ORC_E4M3 || dt == ORC_E5M2) ((uint8_t*)out)[i] = (uint8_t)c;
     else ((uint16_t*)out)[i] = (uint16_t)c;
   }
 }

@@ -158,3 +158,59 @@ def test_encode_special_values():
         assert (c & qnan_mask) == qnan_mask and (c & ~(qnan_mask | 0x8000)) != 0
         assert oracle.encode(dt, -0.0) == 0x8000
         assert oracle.encode(dt, 0.0) == 0
+
+
+# ---------------------------------------------------------------------------------------
+# fp8 encoders (round to nearest even, saturating to the largest finite value)
+# ---------------------------------------------------------------------------------------
+
+FP8_MAXCODE = {"e4m3": 0x7E, "e5m2": 0x7B}
+
+
+def _finite_codes(dt):
+    return [c for c in range(256) if math.isfinite(oracle.decode(dt, c))]
+
+
+@pytest.mark.parametrize("dt", ["e4m3", "e5m2"])
+def test_fp8_encode_round_trips_every_finite_code(dt):
+    for c in _finite_codes(dt):
+        assert oracle.encode(dt, oracle.decode(dt, c)) == c, hex(c)
+
+
+@pytest.mark.parametrize("dt", ["e4m3", "e5m2"])
+def test_fp8_encode_ties_to_even_at_every_midpoint(dt):
+    pos = sorted((oracle.decode(dt, c), c) for c in _finite_codes(dt) if c < 0x80)
+    for (v0, c0), (v1, c1) in zip(pos, pos[1:]):
+        mid = (Fraction(v0) + Fraction(v1)) / 2
+        m = float(mid)
+        assert Fraction(m) == mid  # exact in double
+        even = c0 if c0 % 2 == 0 else c1
+        assert oracle.encode(dt, m) == even, (v0, v1)
+        assert oracle.encode(dt, -m) == even | 0x80
+        step = (v1 - v0) * 1e-6
+        assert oracle.encode(dt, m - step) == c0 and oracle.encode(dt, m + step) == c1
+
+
+@pytest.mark.parametrize("dt", ["e4m3", "e5m2"])
+def test_fp8_encode_saturates_and_keeps_nan(dt):
+    top = FP8_MAXCODE[dt]
+    fmax = oracle.decode(dt, top)
+    assert fmax == (448.0 if dt == "e4m3" else 57344.0)
+    for x in (fmax * 1.0001, fmax * 4, 1e30, math.inf):
+        assert oracle.encode(dt, x) == top and oracle.encode(dt, -x) == top | 0x80
+    assert math.isnan(oracle.decode(dt, oracle.encode(dt, math.nan)))
+    assert oracle.encode(dt, 0.0) == 0x00 and oracle.encode(dt, -0.0) == 0x80
+    # below half the smallest subnormal: zero; just above: the smallest subnormal
+    tiny = oracle.decode(dt, 0x01)
+    assert oracle.encode(dt, tiny * 0.49) == 0x00 and oracle.encode(dt, tiny * 0.51) == 0x01
+
+
+@pytest.mark.parametrize("dt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_encode_matches_torch_in_range(dt, tdt):
+    r = np.random.Generator(np.random.PCG64(17))
+    fmax = oracle.decode(dt, FP8_MAXCODE[dt])
+    x = (r.standard_normal(20000) * np.exp(r.uniform(-12, np.log(fmax), 20000))).astype(np.float32)
+    x = x[np.abs(x) <= fmax].astype(np.float64)
+    ours = oracle.encode_array(dt, x)
+    ref = torch.from_numpy(x).to(torch.float32).to(tdt).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
