@@ -305,6 +305,31 @@ __device__ __forceinline__ uint2 pack4_16(int dt, const float v[4]) {
   return x;
 }
 
+// Four fp32 values as the 4 bytes of 4 OCP fp8 codes (e4m3fn or e5m2), round to nearest even,
+// saturating: magnitudes past the largest finite value (448 / 57344), infinities included,
+// become it; NaN passes the clamp (comparisons with NaN are false) and converts to NaN.
+__device__ __forceinline__ uint32_t pack4_8(int dt, const float v[4]) {
+  const float mx = dt == DT_E4M3 ? 448.f : 57344.f;
+  float c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c[e] = v[e] > mx ? mx : (v[e] < -mx ? -mx : v[e]);
+  int w;
+  if (dt == DT_E4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], w, true);
+  }
+  return (uint32_t)w;
+}
+
+// Four fp32 values to an output element type (not fp32) at p.
+__device__ __forceinline__ void store4(int dt, char* ptr, const float v[4]) {
+  if (dt == DT_E4M3 || dt == DT_E5M2) *(uint32_t*)ptr = pack4_8(dt, v);
+  else *(uint2*)ptr = pack4_16(dt, v);
+}
+
 // Four consecutive 16-bit values (bf16 or f16) to fp32.
 __device__ __forceinline__ void unpack4_16(int dt, uint2 x, float v[4]) {
   if (dt == DT_BF16) {
@@ -317,7 +342,9 @@ __device__ __forceinline__ void unpack4_16(int dt, uint2 x, float v[4]) {
   }
 }
 
-__device__ __forceinline__ int dt_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_NONE ? 0 : 2); }
+__device__ __forceinline__ int dt_bytes(int dt) {
+  return dt == DT_F32 ? 4 : (dt == DT_NONE ? 0 : ((dt == DT_E4M3 || dt == DT_E5M2) ? 1 : 2));
+}
 
 // Complete this wave's LDS operations, then synchronise the workgroup. The "memory"
 // clobber keeps LDS accesses on their side of it.
@@ -846,18 +873,18 @@ struct GemmKernel {
       float d[4] = {v[0] * g[0], v[1] * g[1], v[2] * g[2], v[3] * g[3]};
       float w[4] = {w8[0], w8[1], w8[2], w8[3]};
       if (p.d_dt == DT_F32) *(f32x4*)dp = f32x4{d[0], d[1], d[2], d[3]};
-      else if (p.d_dt != DT_NONE) *(uint2*)dp = pack4_16(p.d_dt, d);
+      else if (p.d_dt != DT_NONE) store4(p.d_dt, dp, d);
       if (p.p_dt == DT_F32) *(f32x4*)pp = f32x4{w[0], w[1], w[2], w[3]};
-      else if (p.p_dt != DT_NONE) *(uint2*)pp = pack4_16(p.p_dt, w);
+      else if (p.p_dt != DT_NONE) store4(p.p_dt, pp, w);
       return;
     }
     if (p.d_dt == DT_F32) *(f32x4*)dp = f32x4{v[0], v[1], v[2], v[3]};
-    else if (p.d_dt != DT_NONE) *(uint2*)dp = pack4_16(p.d_dt, v);
+    else if (p.d_dt != DT_NONE) store4(p.d_dt, dp, v);
     if (p.p_dt != DT_NONE) {
       const f32x8 w8 = act8(p.act, f32x8{v[0], v[1], v[2], v[3], 0.f, 0.f, 0.f, 0.f});
       float w[4] = {w8[0], w8[1], w8[2], w8[3]};
       if (p.p_dt == DT_F32) *(f32x4*)pp = f32x4{w[0], w[1], w[2], w[3]};
-      else *(uint2*)pp = pack4_16(p.p_dt, w);
+      else store4(p.p_dt, pp, w);
     }
   }
 

@@ -44,7 +44,10 @@ static int elem_bytes(int32_t dt) {
 static bool is_input_type(int32_t dt) {
   return dt == DT_F16 || dt == DT_BF16 || dt == DT_E4M3 || dt == DT_E5M2;
 }
-static bool is_output_type(int32_t dt) { return dt == DT_NONE || dt == DT_F16 || dt == DT_BF16 || dt == DT_F32; }
+// C: 16-bit or f32; D and PostAct also OCP fp8 (page 5 is_valid_dtypes), saturating
+static bool is_output_type(int32_t dt, bool c) {
+  return dt == DT_NONE || dt == DT_F16 || dt == DT_BF16 || dt == DT_F32 || (!c && (dt == DT_E4M3 || dt == DT_E5M2));
+}
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -93,7 +96,8 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   const int32_t outs[3] = {d.c, d.d, d.post};
   for (int i = 0; i < 3; ++i) {
     if (outs[i] < 0 || outs[i] > 5) return fail(GEMM_ERR_INVALID_ARG, "unknown dtype %d", outs[i]);
-    if (!is_output_type(outs[i])) return fail(GEMM_ERR_UNSUPPORTED, "C/D/PostAct must be f16, bf16 or f32");
+    if (!is_output_type(outs[i], i == 0))
+      return fail(GEMM_ERR_UNSUPPORTED, "C must be f16, bf16 or f32; D and PostAct f16, bf16, f32, e4m3 or e5m2");
   }
   if (d.d == DT_NONE && d.post == DT_NONE) return fail(GEMM_ERR_INVALID_ARG, "neither D nor PostAct requested");
   if (d.dact != 0 && d.dact != 1) return fail(GEMM_ERR_INVALID_ARG, "dact must be 0 or 1");

@@ -87,7 +87,10 @@ typedef enum {
  *
  * Types: a, b in {F16, BF16, E4M3, E5M2}. 16-bit inputs need a == b; 8-bit inputs may mix
  * E4M3 and E5M2 and must both be GEMM_ROW (K-major) (page 5, is_valid_dtypes).
- * c, d, post in {NONE, F16, BF16, F32}; at least one of d, post is not NONE.
+ * c in {NONE, F16, BF16, F32}; d, post in {NONE, F16, BF16, F32, E4M3, E5M2} (page 5
+ * is_valid_dtypes admits fp8 D); at least one of d, post is not NONE. fp8 outputs round
+ * to nearest even and saturate: magnitudes past the largest finite value (448 for E4M3,
+ * 57344 for E5M2), infinities included, become it; NaN stays NaN.
  * The C term is present iff c != NONE; beta multiplies it (beta = 1 gives +C; beta = 0
  * still reads C, so NaN/inf in C propagate).
  * C, D and PostAct that are present must share one major mode.

@@ -64,6 +64,7 @@ def create(lib, d):
 def test_create_accepts_valid(lib):
     assert create(lib, base_desc()) == _abi.OK
     assert create(lib, base_desc(K=0)) == _abi.OK  # empty K: product is zero
+    assert create(lib, base_desc(d=_abi.DT["e4m3"], post=_abi.DT["e5m2"], ldp=256)) == _abi.OK  # fp8 outputs
     assert create(lib, base_desc(M=0)) == _abi.OK  # empty output
     d = base_desc(a=_abi.DT["e4m3"], b=_abi.DT["e5m2"])
     assert create(lib, d) == _abi.OK
@@ -81,7 +82,8 @@ def test_create_accepts_valid(lib):
     (dict(a=_abi.DT["e4m3"], b=_abi.DT["e4m3"], a_major=_abi.COL), _abi.UNSUPPORTED),
     (dict(a=_abi.DT["f32"], b=_abi.DT["f32"]), _abi.UNSUPPORTED),
     (dict(a=9), _abi.INVALID_ARG),
-    (dict(d=_abi.DT["e4m3"]), _abi.UNSUPPORTED),
+    (dict(c=_abi.DT["e4m3"], ldc=256), _abi.UNSUPPORTED),  # fp8 C
+    (dict(d=_abi.DT["e4m3"], N=264, ldd=264), _abi.ALIGNMENT),  # 264 fp8 bytes: not whole chunks
     (dict(d=0), _abi.INVALID_ARG),  # neither D nor PostAct
     (dict(act=_abi.ACT["relu"]), _abi.INVALID_ARG),  # activation without PostAct
     (dict(act=7, post=2, ldp=256), _abi.INVALID_ARG),

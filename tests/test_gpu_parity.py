@@ -147,6 +147,58 @@ def test_identity_exact():
 
 
 # ---------------------------------------------------------------------------------------
+# fp8 outputs (D / PostAct in e4m3 or e5m2: round to nearest even, saturating)
+# ---------------------------------------------------------------------------------------
+
+def check_fp8(got, want, dt, what):
+    """got: decoded GPU fp8 outputs; want: the oracle's fp64 values. Each output must be the
+    oracle's own encoding of its value, or - where that value lies within fp32 rounding of
+    the midpoint between two fp8 neighbours - the other neighbour."""
+    got = np.asarray(got, dtype=np.float64).ravel()
+    want = np.asarray(want, dtype=np.float64).ravel()
+    enc = oracle.decode_array(dt, oracle.encode_array(dt, want))
+    same = (got == enc) | (np.isnan(got) & np.isnan(enc))
+    near_tie = np.abs(want - (got + enc) / 2) <= 1e-4 * np.abs(want) + 1e-7
+    ok = same | near_tie
+    assert ok.all(), (f"{what}: {(~ok).sum()} outputs off, first at {np.argmax(~ok)}: "
+                      f"got {got[np.argmax(~ok)]} want {want[np.argmax(~ok)]} ({enc[np.argmax(~ok)]})")
+    assert same.mean() > 0.99, f"{what}: only {same.mean():.4f} exact"
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_small_fp8_outputs(tile):
+    inp = small(296, 400, 136, 2, "bf16", c_dt="bf16", d_dt="e4m3", post_dt="e5m2", act="gelu_tanh",
+                alpha=3.0, beta=0.5, seed=60, gen=lambda s, sh, dt: W.normal(s, sh, dt, 0.5))
+    announce(f"fp8 outputs tile={tile}")
+    d, p, _ = run_hip(inp, tile=tile)
+    pre, post = problem_of(inp).all(*oracle_codes(inp))
+    check_fp8(d, pre, "e4m3", "D")
+    check_fp8(p, post, "e5m2", "PostAct")
+
+
+def test_fp8_outputs_exact_saturating_and_nan():
+    r = np.random.Generator(np.random.PCG64(61))
+    M, N, K = 136, 272, 32
+    a = r.integers(-3, 4, size=(1, M, K)).astype(np.float64)
+    b = r.integers(-3, 4, size=(1, N, K)).astype(np.float64)
+    c = r.integers(-8, 9, size=(1, M, N)).astype(np.float64)
+    c[0, 5, 7] = np.nan
+    c[0, 9, 11] = np.inf
+    c[0, 10, 12] = -np.inf
+    for d_dt, p_dt in (("e4m3", "e5m2"), ("e5m2", "e4m3")):
+        inp = W.Inputs("fp8out", M, N, K, 1, "bf16", "bf16", W.to_dtype(a, "bf16"), W.to_dtype(b, "bf16"),
+                       C=W.to_dtype(c, "f32"), c_dt="f32", d_dt=d_dt, post_dt=p_dt, act="relu",
+                       alpha=8.0, beta=1.0)  # |8 acc| up to 2304: past e4m3's 448
+        d, p, _ = run_hip(inp)
+        pre, post = problem_of(inp).all(*oracle_codes(inp))
+        for got, want, dt in ((d, pre, d_dt), (p, post, p_dt)):
+            enc = oracle.decode_array(dt, oracle.encode_array(dt, want.ravel())).reshape(want.shape)
+            assert np.array_equal(np.isnan(got), np.isnan(enc))
+            assert np.array_equal(got[~np.isnan(got)], enc[~np.isnan(enc)]), dt
+        assert np.isnan(d[0, 5, 7]) and d[0, 9, 11] == (448.0 if d_dt == "e4m3" else 57344.0)
+
+
+# ---------------------------------------------------------------------------------------
 # activation backward (dact): D = (alpha A x B) * act'(C), PostAct = act(C)
 # ---------------------------------------------------------------------------------------
 
