@@ -33,6 +33,9 @@ class _Problem(ctypes.Structure):
         ("has_c", ctypes.c_int32), ("act", ctypes.c_int32), ("varlen", ctypes.c_int32),
         ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
         ("dact", ctypes.c_int32),
+        ("varlen_k", ctypes.c_int32),
+        ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32)),
+        ("a_idx", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -141,7 +144,13 @@ class Problem:
 
     def __init__(self, M, N, K, L, a_dt, b_dt, a_kmajor=True, b_kmajor=True, lda=None, ldb=None,
                  sa=0, sb=0, c_dt="none", c_nmajor=True, ldc=None, sc=0, alpha=1.0, beta=1.0,
-                 act="none", cu_seqlens=None, dact=False):
+                 act="none", cu_seqlens=None, dact=False, cu_seqlens_k=None, a_idx=None):
+        """Varlen-K: cu_seqlens_k (L+1 entries) splits K into groups, A (M, K) and B (N, K)
+        have no batch index, K is A's and B's total K extent. a_idx (varlen-M or varlen-K
+        only): the A row of each global output row, or the A column of each global k."""
+        assert cu_seqlens is None or cu_seqlens_k is None, "varlen in M or in K, not both"
+        assert a_idx is None or cu_seqlens is not None or cu_seqlens_k is not None, \
+            "gathered A needs varlen-M or varlen-K"
         self.M, self.N, self.K, self.L = M, N, K, L
         self.dact = bool(dact)
         assert not self.dact or c_dt != "none", "the activation-backward epilogue reads C"
@@ -153,6 +162,8 @@ class Problem:
         self.sa, self.sb, self.sc = sa, sb, sc
         self.alpha, self.beta, self.act = alpha, beta, act
         self.cu_seqlens = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        self.cu_seqlens_k = None if cu_seqlens_k is None else np.ascontiguousarray(cu_seqlens_k, dtype=np.int32)
+        self.a_idx = None if a_idx is None else np.ascontiguousarray(a_idx, dtype=np.int32)
 
     def _struct(self):
         s = _Problem()
@@ -169,6 +180,12 @@ class Problem:
         if self.cu_seqlens is not None:
             assert len(self.cu_seqlens) == self.L + 1
             s.cu_seqlens = self.cu_seqlens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        s.varlen_k = int(self.cu_seqlens_k is not None)
+        if self.cu_seqlens_k is not None:
+            assert len(self.cu_seqlens_k) == self.L + 1
+            s.cu_seqlens_k = self.cu_seqlens_k.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        if self.a_idx is not None:
+            s.a_idx = self.a_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         return s
 
     @staticmethod
@@ -199,7 +216,7 @@ class Problem:
         return pre, post
 
     def all(self, A, B, C, nthreads=0):
-        """pre, post (fp64): [L, M, N], or [M, N] over global rows in varlen mode."""
+        """pre, post (fp64): [L, M, N], or [M, N] over global rows in varlen-M mode."""
         shape = (self.M, self.N) if self.cu_seqlens is not None else (self.L, self.M, self.N)
         pre = np.empty(shape); post = np.empty(shape)
         s = self._struct()
@@ -213,16 +230,25 @@ def problem_from(inp, act=None, alpha=None, beta=None):
     alpha, beta, act, cu_seqlens, with A / B / C torch views whose strides give the layout)."""
     A, B = inp.A, inp.B
     varlen = inp.cu_seqlens is not None
-    if varlen:
+    cu_k = getattr(inp, "cu_seqlens_k", None)
+    a_idx = getattr(inp, "a_idx", None)
+    if varlen or cu_k is not None:  # A is (rows, K) with no batch index
         a_k = A.stride(1) == 1
         lda = A.stride(0) if a_k else A.stride(1)
-        sa, L = 0, B.shape[0]
+        sa = 0
+        L = B.shape[0] if varlen else len(cu_k) - 1
     else:
         a_k = A.stride(2) == 1
         lda = A.stride(1) if a_k else A.stride(2)
         sa, L = A.stride(0), A.shape[0]
-    b_k = B.stride(2) == 1
-    ldb = B.stride(1) if b_k else B.stride(2)
+    if cu_k is not None:  # B is (N, K) with no batch index
+        b_k = B.stride(1) == 1
+        ldb = B.stride(0) if b_k else B.stride(1)
+        sb = 0
+    else:
+        b_k = B.stride(2) == 1
+        ldb = B.stride(1) if b_k else B.stride(2)
+        sb = B.stride(0)
     kw = {}
     if inp.C is not None:
         C = inp.C if inp.C.dim() == 3 else inp.C.unsqueeze(0)
@@ -230,11 +256,11 @@ def problem_from(inp, act=None, alpha=None, beta=None):
         kw = dict(c_dt=inp.c_dt, c_nmajor=c_n, ldc=C.stride(1) if c_n else C.stride(2),
                   sc=0 if varlen else C.stride(0))
     return Problem(inp.M, inp.N, inp.K, L, inp.a_dt, inp.b_dt, a_kmajor=a_k, b_kmajor=b_k,
-                   lda=lda, ldb=ldb, sa=sa, sb=B.stride(0),
+                   lda=lda, ldb=ldb, sa=sa, sb=sb,
                    alpha=inp.alpha if alpha is None else alpha,
                    beta=inp.beta if beta is None else beta,
                    act=inp.act if act is None else act, cu_seqlens=inp.cu_seqlens,
-                   dact=getattr(inp, "dact", False), **kw)
+                   dact=getattr(inp, "dact", False), cu_seqlens_k=cu_k, a_idx=a_idx, **kw)
 
 
 # ---------------------------------------------------------------------------------------

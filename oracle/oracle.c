@@ -218,7 +218,15 @@ double orc_dact(int act, double x) {
  *   x_nmajor = 1: X[l*sx + m*ldx + n]          x_nmajor = 0: X[l*sx + n*ldx + m]
  * Variable-length M (grouped): cu_seqlens has L+1 entries, group g owns global rows
  * [cu[g], cu[g+1]); A, C, D, PostAct are indexed by the global row with batch 0, and
- * B by the group g (page 5, the varlen-M offsets of A, B and D in GemmSm90.kernel). */
+ * B by the group g (page 5, the varlen-M offsets of A, B and D in GemmSm90.kernel).
+ * Variable-length K (grouped, page 5 GemmSm90.kernel and the torch-vendored gemm_sm90.py
+ * page: cu_seqlens_k offsets the K coordinate of A and B by cu_seqlens_k[l] and the group's
+ * K extent is cu_seqlens_k[l+1] - cu_seqlens_k[l]): cu_seqlens_k has L+1 entries, A is
+ * (m, total_k) and B is (n, total_k) with no batch index, C / D / PostAct are (l, m, n);
+ * group l sums k over [cu_k[l], cu_k[l+1]), an empty range giving acc = 0.
+ * Gathered A (mAIdx on the same pages; the gather copies of load_AB_gather_A and
+ * _make_gather_A_copy): with varlen-M, the A row read for global output row m is
+ * a_idx[m]; with varlen-K, the A column read for global k is a_idx[k]. */
 typedef struct {
   int64_t M, N, K, L;
   int32_t a_dt, b_dt, c_dt;
@@ -231,6 +239,9 @@ typedef struct {
   int32_t varlen;
   const int32_t* cu_seqlens; /* host array, L+1 entries, when varlen */
   int32_t dact;              /* 1: activation-backward epilogue, C holds the pre-activation */
+  int32_t varlen_k;          /* 1: grouped K, cu_seqlens_k given */
+  const int32_t* cu_seqlens_k; /* host array, L+1 entries, when varlen_k */
+  const int32_t* a_idx;      /* host array or NULL: gathered A rows (varlen-M) / columns (varlen-K) */
 } orc_problem;
 
 static double load_elem(const void* base, int dt, int64_t idx) {
@@ -259,14 +270,23 @@ static int64_t group_of_row(const orc_problem* p, int64_t r) {
 static void elem(const orc_problem* p, const void* A, const void* B, const void* C, int64_t l,
                  int64_t m, int64_t n, double* pre, double* post) {
   int64_t lb = l;   /* batch index used for B */
-  int64_t lx = l;   /* batch index used for A, C */
+  int64_t la = l;   /* batch index used for A */
+  int64_t lx = l;   /* batch index used for C */
+  int64_t k_lo = 0, k_hi = p->K;
   if (p->varlen) {
     lb = group_of_row(p, m);
-    lx = 0;
+    la = lx = 0;
   }
+  if (p->varlen_k) {
+    k_lo = p->cu_seqlens_k[l];
+    k_hi = p->cu_seqlens_k[l + 1];
+    la = lb = 0;
+  }
+  int64_t ma = (p->a_idx && p->varlen) ? (int64_t)p->a_idx[m] : m; /* the A row read */
   double acc = 0.0;
-  for (int64_t k = 0; k < p->K; ++k) {
-    int64_t ia = lx * p->sa + (p->a_kmajor ? m * p->lda + k : k * p->lda + m);
+  for (int64_t k = k_lo; k < k_hi; ++k) {
+    int64_t ka = (p->a_idx && p->varlen_k) ? (int64_t)p->a_idx[k] : k; /* the A column read */
+    int64_t ia = la * p->sa + (p->a_kmajor ? ma * p->lda + ka : ka * p->lda + ma);
     int64_t ib = lb * p->sb + (p->b_kmajor ? n * p->ldb + k : k * p->ldb + n);
     acc += load_elem(A, p->a_dt, ia) * load_elem(B, p->b_dt, ib);
   }
