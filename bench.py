@@ -23,7 +23,8 @@ METRIC = "GEMM TFLOPS and % of MFMA peak at 8192^3 bf16/fp8; varlen-M grouped TF
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "e5m2": 5000.0}
 HBM_PEAK_GBS = 8000.0
 PRIMARY = "square_8192_bf16"
-SECONDARY = ["fp8_8192", "varlen_moe", "square_8192_f16", "act_4096", "batched_2048", "dact_4096"]
+SECONDARY = ["fp8_8192", "varlen_moe", "square_8192_f16", "act_4096", "batched_2048", "dact_4096",
+             "varlen_k_moe", "varlen_moe_gather"]
 
 
 def source_hash():
@@ -40,9 +41,13 @@ def algorithmic_bytes(inp):
     """Minimum HBM bytes: read A, B (and C) once, write the outputs once."""
     es = {"f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e5m2": 1, "none": 0}
     if inp.varlen:
-        a = inp.M * inp.K * es[inp.a_dt]
+        a = (inp.A.shape[0] if inp.a_idx is not None else inp.M) * inp.K * es[inp.a_dt]
         b = inp.L * inp.N * inp.K * es[inp.b_dt]
         mn = inp.M * inp.N
+    elif inp.cu_seqlens_k is not None:
+        a = inp.M * inp.K * es[inp.a_dt]
+        b = inp.N * inp.K * es[inp.b_dt]
+        mn = inp.L * inp.M * inp.N
     else:
         a = inp.L * inp.M * inp.K * es[inp.a_dt]
         b = inp.L * inp.N * inp.K * es[inp.b_dt]
@@ -60,11 +65,31 @@ def setup(name, **tuning):
     D = out_like(inp, inp.d_dt) if inp.d_dt != "none" else None
     P = out_like(inp, inp.post_dt) if inp.post_dt != "none" else None
     cu = torch.from_numpy(inp.cu_seqlens).to("cuda") if inp.varlen else None
+    cuk = torch.from_numpy(inp.cu_seqlens_k).to("cuda") if inp.cu_seqlens_k is not None else None
+    idx = torch.from_numpy(inp.a_idx).to("cuda") if inp.a_idx is not None else None
     if inp.dact:
         tuning = dict(tuning, dact=True)
-    plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu, **tuning)
+    plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu, cuk, idx, **tuning)
     args = (A, B, C, D, P, None, None, cu)
+    if cuk is not None or idx is not None:
+        plan = _Bound(plan, cu_seqlens_k=cuk, a_idx=idx)
     return inp, plan, args
+
+
+class _Bound:
+    """A plan whose run() carries the varlen-K / gather device arrays."""
+
+    def __init__(self, plan, **extra):
+        self.plan, self.extra = plan, extra
+
+    def run(self, *args):
+        self.plan.run(*args, **self.extra)
+
+    def grid(self):
+        return self.plan.grid()
+
+    def raster_along_n(self):
+        return self.plan.raster_along_n()
 
 
 SETTLE_S = 0.3  # untimed running before the warmup steps: the clock ramps up over ~0.1 s

@@ -10,7 +10,10 @@ fallback path: if the library is missing, importing the binding's entry points r
 Tensors follow the wrapper convention of quack-kernels (0.1.10 -> 0.2.0 diff, page 5,
 quack/dense_gemm_sm90.py, gemm_sm90): A (l, m, k), B (l, n, k), C / D / PostAct (l, m, n),
 with the major mode of each read from its strides; 2-D tensors mean l = 1. In varlen-M
-mode (cu_seqlens_m given) A is (M, K), B is (G, N, K), C / D / PostAct are (M, N).
+mode (cu_seqlens_m given) A is (M, K), B is (G, N, K), C / D / PostAct are (M, N); with
+a_idx (gathered A) A is (rows, K) and output row r reads A row a_idx[r]. In varlen-K mode
+(cu_seqlens_k given; the same pages' grouped K) A is (M, K), B is (N, K) and C / D /
+PostAct are (G, M, N), group g summing k over [cu_seqlens_k[g], cu_seqlens_k[g+1]).
 """
 import ctypes
 
@@ -61,13 +64,25 @@ def _bstride(t):
 
 def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none",
              varlen=False, tile=None, group_m=0, max_ctas=0, xcd_remap=0,
-             tail_split=0, raster_order=0, dact=False):
-    """Build the gemm_desc for these tensors (no GPU work)."""
+             tail_split=0, raster_order=0, dact=False, varlen_k=0, gather=False):
+    """Build the gemm_desc for these tensors (no GPU work). varlen_k: the number of K groups
+    (len(cu_seqlens_k) - 1), or 0. gather: A rows are read through a_idx (varlen-M)."""
     d = _abi.GemmDesc()
-    if varlen:
+    if varlen_k:
         M, K = A.shape
+        N, K2 = B.shape
+        L = varlen_k
+        A3, B3 = A.unsqueeze(0), B.unsqueeze(0)
+        C3, D3, P3 = (_as3(x) for x in (C, D, PostAct))
+        for name, x in (("C", C3), ("D", D3), ("PostAct", P3)):
+            if x is not None and x.shape[0] != L:
+                raise ValueError(f"{name}: expected {L} batches (one per K group)")
+    elif varlen:
+        rows_a, K = A.shape
         G, N, K2 = B.shape
         L = G
+        out = D if D is not None else PostAct
+        M = out.shape[0] if gather else rows_a
         A3, B3 = A.unsqueeze(0), B
         C3, D3, P3 = (None if x is None else x.unsqueeze(0) for x in (C, D, PostAct))
     else:
@@ -85,7 +100,7 @@ def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none"
     d.a, d.b, d.c, d.d, d.post = (DT[_dt(x)] for x in (A, B, C, D, PostAct))
     d.a_major, d.lda = _major_ld(A3, "A")
     d.b_major, d.ldb = _major_ld(B3, "B")
-    d.sa, d.sb = (0 if varlen else _bstride(A3)), _bstride(B3)
+    d.sa, d.sb = (0 if (varlen or varlen_k) else _bstride(A3)), (0 if varlen_k else _bstride(B3))
     for x, mf, lf, sf in ((C3, "c_major", "ldc", "sc"), (D3, "d_major", "ldd", "sd"),
                           (P3, "post_major", "ldp", "sp")):
         if x is not None:
@@ -101,6 +116,9 @@ def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none"
     d.group_m, d.max_ctas, d.xcd_remap, d.tail_split = group_m, max_ctas, xcd_remap, tail_split
     d.raster_order = raster_order
     d.dact = 1 if dact else 0
+    d.varlen_k = 1 if varlen_k else 0
+    d.gather_a = 1 if gather else 0
+    d.gather_rows = A.shape[0] if gather else 0
     return d
 
 
@@ -121,12 +139,18 @@ def _stream(stream):
 
 
 class Plan:
-    """A validated plan for one problem shape (host memory; reusable across calls)."""
+    """A validated plan for one problem shape (host memory; reusable across calls).
+    cu_seqlens_k / a_idx select varlen-K / gathered A (their values are read at run time;
+    only their presence and, for varlen-K, the group count matter to the plan)."""
 
     def __init__(self, A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none",
-                 cu_seqlens_m=None, **tuning):
+                 cu_seqlens_m=None, cu_seqlens_k=None, a_idx=None, **tuning):
         self.varlen = cu_seqlens_m is not None
-        self.desc = describe(A, B, C, D, PostAct, alpha, beta, act, self.varlen, **tuning)
+        self.varlen_k = cu_seqlens_k is not None
+        self.gather = a_idx is not None
+        self.desc = describe(A, B, C, D, PostAct, alpha, beta, act, self.varlen, **tuning,
+                             varlen_k=(cu_seqlens_k.numel() - 1) if self.varlen_k else 0,
+                             gather=self.gather)
         self.handle = gemm_create(self.desc)
         self._lib = _abi.load()
 
@@ -137,16 +161,32 @@ class Plan:
             self.handle = None
 
     def run(self, A, B, C=None, D=None, PostAct=None, alpha_dev=None, beta_dev=None,
-            cu_seqlens_m=None, stream=None, tile_log=None, max_iters=0, tile_counters=None):
+            cu_seqlens_m=None, stream=None, tile_log=None, max_iters=0, tile_counters=None,
+            cu_seqlens_k=None, a_idx=None):
         """Enqueue on `stream` (default: torch's current stream). alpha_dev / beta_dev:
         optional fp32 device tensors of one element, read by the kernel. tile_counters: an
         int32 device tensor of 8 zeros selects the dynamic schedule (gemm_run_dynamic; the
-        kernel leaves it zero again)."""
-        args = [self.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(PostAct), _ptr(alpha_dev),
-                _ptr(beta_dev), _ptr(cu_seqlens_m)]
+        kernel leaves it zero again). Varlen-K and gathered-A plans run through gemm_run_ex
+        with cu_seqlens_k / a_idx (int32 device tensors)."""
         if tile_counters is not None:
             if tile_counters.dtype != torch.int32 or tile_counters.numel() < 8 or not tile_counters.is_cuda:
                 raise ValueError("tile_counters: int32 device tensor of at least 8 elements")
+        for name, x in (("cu_seqlens_m", cu_seqlens_m), ("cu_seqlens_k", cu_seqlens_k), ("a_idx", a_idx)):
+            if x is not None and (x.dtype != torch.int32 or not x.is_cuda or not x.is_contiguous()):
+                raise ValueError(f"{name}: contiguous int32 device tensor expected")
+        if self.varlen_k or self.gather:
+            if tile_log is not None:
+                raise ValueError("the tile log is not offered for varlen-K / gathered-A plans")
+            a = _abi.GemmArgs()
+            a.A, a.B, a.C, a.D, a.PostAct = (None if t is None else t.data_ptr() for t in (A, B, C, D, PostAct))
+            a.alpha_dev, a.beta_dev = (None if t is None else t.data_ptr() for t in (alpha_dev, beta_dev))
+            a.cu_seqlens_m, a.cu_seqlens_k, a.a_idx, a.tile_counters = (
+                None if t is None else t.data_ptr() for t in (cu_seqlens_m, cu_seqlens_k, a_idx, tile_counters))
+            _abi.check(self._lib.gemm_run_ex(self.handle, ctypes.byref(a), _stream(stream)))
+            return
+        args = [self.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(PostAct), _ptr(alpha_dev),
+                _ptr(beta_dev), _ptr(cu_seqlens_m)]
+        if tile_counters is not None:
             st = self._lib.gemm_run_dynamic(*args, _ptr(tile_counters), _ptr(tile_log), int(max_iters),
                                             _stream(stream))
         elif tile_log is not None:
@@ -174,10 +214,11 @@ class Plan:
 
 
 def gemm(A, B, D=None, C=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu_seqlens_m=None,
-         alpha_dev=None, beta_dev=None, stream=None, **tuning):
+         alpha_dev=None, beta_dev=None, stream=None, cu_seqlens_k=None, a_idx=None, **tuning):
     """One-shot call: plan (validated on the host) and enqueue. Outputs are written in place."""
-    p = Plan(A, B, C, D, PostAct, alpha, beta, act, cu_seqlens_m, **tuning)
-    p.run(A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, stream)
+    p = Plan(A, B, C, D, PostAct, alpha, beta, act, cu_seqlens_m, cu_seqlens_k, a_idx, **tuning)
+    p.run(A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, stream, cu_seqlens_k=cu_seqlens_k,
+          a_idx=a_idx)
     return D if D is not None else PostAct
 
 

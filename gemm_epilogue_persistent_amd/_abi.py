@@ -28,7 +28,13 @@ class GemmDesc(ctypes.Structure):
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
         ("group_m", ctypes.c_int32), ("max_ctas", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
         ("tail_split", ctypes.c_int32), ("raster_order", ctypes.c_int32), ("dact", ctypes.c_int32),
+        ("varlen_k", ctypes.c_int32), ("gather_a", ctypes.c_int32), ("gather_rows", ctypes.c_int64),
     ]
+
+
+class GemmArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("A", "B", "C", "D", "PostAct", "alpha_dev", "beta_dev",
+                                               "cu_seqlens_m", "cu_seqlens_k", "a_idx", "tile_counters")]
 
 
 class GemmError(RuntimeError):
@@ -56,6 +62,8 @@ def load():
         lib.gemm_run_logged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
         lib.gemm_run_dynamic.restype = ctypes.c_int
         lib.gemm_run_dynamic.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
+        lib.gemm_run_ex.restype = ctypes.c_int
+        lib.gemm_run_ex.argtypes = [vp, ctypes.POINTER(GemmArgs), vp]
         lib.gemm_destroy.restype = ctypes.c_int
         lib.gemm_destroy.argtypes = [vp]
         lib.gemm_plan_grid.restype = ctypes.c_int

@@ -15,8 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm_mi355x.so")
-UNITS = ["plan.cpp", "gemm_api.hip", "inst_f16.hip", "inst_bf16.hip", "inst_fp8.hip", "inst_f16_dact.hip",
-         "inst_bf16_dact.hip", "inst_fp8_dact.hip", "probe.hip"]
+# one unit per (operand type, epilogue kind, varlen mode) family of kernels
+UNITS = ["plan.cpp", "gemm_api.hip", "probe.hip"] + [
+    f"inst_{op}_{fam}.hip" for op in ("f16", "bf16", "fp8") for fam in ("fwd", "vm", "vk", "dact", "dact_vm")]
 
 
 def hipcc() -> str:

@@ -1,4 +1,4 @@
-// gemm_run / gemm_run_logged and the device FastDivmod self-check (C ABI).
+// gemm_run / gemm_run_ex / gemm_run_logged / gemm_run_dynamic and the device FastDivmod self-check (C ABI).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,18 +32,31 @@ static gemm_status current_cus(int32_t* cus) {
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+template <int OP>
+static hipError_t launch_op(const KernelKey& key, const KParams& k, hipStream_t s) {
+  if (key.dact) {
+    if (key.varlen == 0) return launch_family<OP, true, 0>(key, k, s);
+    if (key.varlen == 1) return launch_family<OP, true, 1>(key, k, s);
+    return hipErrorInvalidValue;
+  }
+  if (key.varlen == 0) return launch_family<OP, false, 0>(key, k, s);
+  if (key.varlen == 1) return launch_family<OP, false, 1>(key, k, s);
+  return launch_family<OP, false, 2>(key, k, s);
+}
+
 static hipError_t launch_key(const KernelKey& key, const KParams& k, hipStream_t s) {
-  const bool da = key.dact != 0;
   switch (key.op) {
-    case OP_F16: return da ? launch_family<OP_F16, true>(key, k, s) : launch_family<OP_F16, false>(key, k, s);
-    case OP_BF16: return da ? launch_family<OP_BF16, true>(key, k, s) : launch_family<OP_BF16, false>(key, k, s);
-    default: return da ? launch_family<OP_FP8, true>(key, k, s) : launch_family<OP_FP8, false>(key, k, s);
+    case OP_F16: return launch_op<OP_F16>(key, k, s);
+    case OP_BF16: return launch_op<OP_BF16>(key, k, s);
+    default: return launch_op<OP_FP8>(key, k, s);
   }
 }
 
+// cu: cu_seqlens_m (varlen-M plans) or cu_seqlens_k (varlen-K plans); a_idx: gathered A rows.
 static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
                             void* Post, const float* alpha_dev, const float* beta_dev, const int32_t* cu,
-                            int32_t* counters, int32_t* tile_log, int32_t max_iters, void* stream) {
+                            const int32_t* a_idx, int32_t* counters, int32_t* tile_log, int32_t max_iters,
+                            void* stream) {
   if (!plan) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: NULL plan");
   // nothing to compute: no tiles (dense) or no rows / columns / groups (varlen)
   const bool empty = plan->varlen ? (plan->base.M == 0 || plan->base.N == 0 || plan->L == 0) : plan->T == 0;
@@ -53,6 +66,10 @@ static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B,
   if (plan->has_d != (D != nullptr)) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: D must be given iff the plan has a D type");
   if (plan->has_p != (Post != nullptr)) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: PostAct must be given iff the plan has a PostAct type");
   if (plan->varlen && !cu) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: cu_seqlens_m is required for a varlen plan");
+  if (plan->varlen_k && !cu) return fail(GEMM_ERR_INVALID_ARG, "gemm_run_ex: cu_seqlens_k is required for a varlen-K plan");
+  if (plan->gather && !a_idx) return fail(GEMM_ERR_INVALID_ARG, "gemm_run_ex: a_idx is required for a gathered-A plan");
+  if (((uintptr_t)cu & 3u) != 0 || ((uintptr_t)a_idx & 3u) != 0)
+    return fail(GEMM_ERR_ALIGNMENT, "gemm_run: cu_seqlens / a_idx not 4-byte aligned");
   if (plan->key.dact && beta_dev) return fail(GEMM_ERR_INVALID_ARG, "gemm_run: a dact plan takes no beta");
   if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D) || !aligned16(Post))
     return fail(GEMM_ERR_ALIGNMENT, "gemm_run: operand pointers must be 16-byte aligned");
@@ -68,6 +85,7 @@ static gemm_status run_impl(const gemm_plan* plan, const void* A, const void* B,
   k.alpha_ptr = alpha_dev;
   k.beta_ptr = beta_dev;
   k.cu_seqlens = cu;
+  k.a_idx = a_idx;
   k.tile_counters = counters;
   k.tile_log = tile_log;
   k.tile_log_iters = tile_log ? max_iters : 0;
@@ -127,13 +145,36 @@ __global__ __launch_bounds__(256) void fastdivmod_check_kernel(uint32_t d_lo, ui
   if (local) atomicAdd(bad, local);
 }
 
+// The entry points of the C ABI that predate varlen-K and gathered A take no place for their
+// device arrays: such plans must go through gemm_run_ex.
+static gemm_status legacy_ok(const gemm_plan* plan, const char* fn) {
+  if (plan && (plan->varlen_k || plan->gather))
+    return fail(GEMM_ERR_INVALID_ARG, "%s: varlen-K and gathered-A plans run through gemm_run_ex", fn);
+  return GEMM_OK;
+}
+
 }  // namespace gep
 
 extern "C" {
 
 gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D, void* PostAct,
                      const float* alpha_dev, const float* beta_dev, const int32_t* cu_seqlens_m, void* stream) {
-  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, nullptr, 0, stream);
+  if (gep::legacy_ok(plan, "gemm_run") != GEMM_OK) return GEMM_ERR_INVALID_ARG;
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, nullptr, nullptr, 0,
+                       stream);
+}
+
+gemm_status gemm_run_ex(const gemm_plan* plan, const gemm_args* a, void* stream) {
+  if (!a) return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_ex: NULL args");
+  if (plan && !plan->varlen_k && a->cu_seqlens_k)
+    return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_ex: cu_seqlens_k given to a plan without varlen_k");
+  if (plan && !plan->varlen && a->cu_seqlens_m)
+    return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_ex: cu_seqlens_m given to a plan without varlen_m");
+  if (plan && !plan->gather && a->a_idx)
+    return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_ex: a_idx given to a plan without gather_a");
+  const int32_t* cu = (plan && plan->varlen_k) ? a->cu_seqlens_k : a->cu_seqlens_m;
+  return gep::run_impl(plan, a->A, a->B, a->C, a->D, a->PostAct, a->alpha_dev, a->beta_dev, cu, a->a_idx,
+                       a->tile_counters, nullptr, 0, stream);
 }
 
 gemm_status gemm_run_dynamic(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
@@ -141,16 +182,18 @@ gemm_status gemm_run_dynamic(const gemm_plan* plan, const void* A, const void* B
                              const int32_t* cu_seqlens_m, int32_t* tile_counters, int32_t* tile_log,
                              int32_t max_iters, void* stream) {
   if (!tile_counters) return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_dynamic: NULL tile_counters");
-  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, tile_counters, tile_log,
-                       max_iters, stream);
+  if (gep::legacy_ok(plan, "gemm_run_dynamic") != GEMM_OK) return GEMM_ERR_INVALID_ARG;
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, tile_counters,
+                       tile_log, max_iters, stream);
 }
 
 gemm_status gemm_run_logged(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
                             void* PostAct, const float* alpha_dev, const float* beta_dev,
                             const int32_t* cu_seqlens_m, int32_t* tile_log, int32_t max_iters, void* stream) {
   if (!tile_log) return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_logged: NULL tile_log");
-  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, tile_log, max_iters,
-                       stream);
+  if (gep::legacy_ok(plan, "gemm_run_logged") != GEMM_OK) return GEMM_ERR_INVALID_ARG;
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, nullptr, tile_log,
+                       max_iters, stream);
 }
 
 gemm_status gemm_fastdivmod_check(uint32_t d_lo, uint32_t d_hi, uint32_t n_count, unsigned long long* bad_dev,

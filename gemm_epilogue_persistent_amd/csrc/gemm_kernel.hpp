@@ -168,6 +168,24 @@ struct TileLoader {
     }
   }
 
+  // K-major operand with gathered rows: tile row r reads operand row ridx[r] (a row index
+  // in [0, nrows); others read as zero), so offsets count from the operand's base, not the
+  // tile's (the plan keeps the operand below 2^31 bytes).
+  __device__ __forceinline__ void init_gather(int wave, int lane, int rows_valid, int64_t ld_bytes, int K,
+                                              const int32_t* ridx, int32_t nrows) {
+    static_assert(KMAJ, "gathered rows need a K-major operand");
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q) {
+      const int blk = q * NW + wave;
+      const int row = blk * (1024 / kRowBytes) + lane / kChunks;
+      const int c = PAD ? lane % kChunks : (lane % kChunks) ^ kswz(row);
+      const int32_t src = row < rows_valid ? ridx[row] : -1;
+      offv[q] = (uint32_t)src < (uint32_t)nrows ? (uint32_t)(src * ld_bytes + c * 16) : kOOB;
+    }
+    if constexpr (PAD) klim = K - (lane % kChunks) * (16 / ES);
+    else klim = K - (((lane % kChunks) ^ kswz(wave * (1024 / kRowBytes) + lane / kChunks)) * (16 / ES));
+  }
+
   // Global -> registers, chunk Q of the k-tile starting at element k0 of K. Chunks at
   // k >= K (the K tail, and whole k-tiles past the end) read as zero.
   template <int Q>
@@ -397,6 +415,7 @@ __device__ __forceinline__ void raster(const KParams& p, uint32_t r, uint32_t ta
 // Everything the loop needs about one output tile.
 struct TileInfo {
   int l, m0, n0, row_end;
+  int klen;            // K extent of the tile's problem (varlen-K: of its group)
   int mb, nb;          // block coordinates inside the batch / group
   const char* a_tile;  // first byte of the tile's A rows (K-major) / columns (M-major)
   const char* b_tile;
@@ -404,8 +423,14 @@ struct TileInfo {
 };
 
 
-template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, bool VARLEN, int NW, bool DACT = false>
+// VM: 0 dense batched, 1 varlen-M (cu_seqlens splits the rows), 2 varlen-K (cu_seqlens
+// splits K; one output batch per group). GA: A rows gathered through a_idx (varlen-M).
+template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, int VM, int NW, bool DACT = false,
+          bool GA = false>
 struct GemmKernel {
+  static constexpr bool VARLEN = VM == 1;
+  static constexpr bool VARK = VM == 2;
+  static_assert(!GA || (VARLEN && A_K), "gathered A rows: varlen-M with a K-major A");
   // NW wave64s in a 2 x (NW/2) grid over the output tile
   static constexpr int kThreads = NW * 64;
   using Op = Mfma<OP, FA, FB>;
@@ -528,10 +553,19 @@ struct GemmKernel {
       ti.m0 += (u & 1) * BM;
       ti.n0 += ((u >> 1) & 1) * BN;
     }
-    const int64_t a_lb = VARLEN ? 0 : (int64_t)ti.l * p.sa;
-    const int64_t b_lb = (int64_t)ti.l * p.sb;
-    const int64_t a_off = (a_lb + (A_K ? (int64_t)ti.m0 * p.lda : (int64_t)ti.m0)) * kES;
-    const int64_t b_off = (b_lb + (B_K ? (int64_t)ti.n0 * p.ldb : (int64_t)ti.n0)) * kES;
+    // varlen-K: the group's K range [cu[l], cu[l+1]) offsets A and B along K
+    int64_t kb = 0;
+    ti.klen = p.K;
+    if constexpr (VARK) {
+      kb = p.cu_seqlens[ti.l];
+      ti.klen = p.cu_seqlens[ti.l + 1] - (int)kb;
+    }
+    const int64_t a_lb = (VARLEN || VARK) ? 0 : (int64_t)ti.l * p.sa;
+    const int64_t b_lb = VARK ? 0 : (int64_t)ti.l * p.sb;
+    // gathered A: the loader's offsets count from A's base (rows come from a_idx)
+    const int64_t a_off =
+        GA ? 0 : (a_lb + (A_K ? (int64_t)ti.m0 * p.lda + kb : kb * p.lda + (int64_t)ti.m0)) * kES;
+    const int64_t b_off = (b_lb + (B_K ? (int64_t)ti.n0 * p.ldb + kb : kb * p.ldb + (int64_t)ti.n0)) * kES;
     ti.a_tile = (const char*)p.A + a_off;
     ti.b_tile = (const char*)p.B + b_off;
     ti.a_room = p.a_bytes - a_off;
@@ -1057,10 +1091,6 @@ struct GemmKernel {
 
     const float alpha = p.alpha_ptr ? *p.alpha_ptr : p.alpha;
     const float beta = p.beta_ptr ? *p.beta_ptr : p.beta;
-    // k-tiles, run in pairs (the stages alternate): an odd count gets one more k-tile past
-    // K, whose loads read zeros and which adds nothing
-    const int nk = (((p.K + kBK - 1) / kBK) + 1) & ~1;
-
     LA la;
     LB lb;
     Frag fa[2][kMI], fb[2][kNI];
@@ -1068,8 +1098,9 @@ struct GemmKernel {
     // a tile's first k-tile goes into the staging registers as early as possible
     auto begin_tile = [&](int t) {
       ti = decode(p, t, gstart, t_lo);
-      la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES, p.K);
-      lb.init(wave, lane, p.N - ti.n0, p.ldb * kES, p.K);
+      if constexpr (GA) la.init_gather(wave, lane, ti.row_end - ti.m0, p.lda * kES, ti.klen, p.a_idx + ti.m0, p.a_rows);
+      else la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES, ti.klen);
+      lb.init(wave, lane, p.N - ti.n0, p.ldb * kES, ti.klen);
       if constexpr (!kDMA) load_all(la, lb, kt_src(p, ti, 0));
     };
     // dynamic schedule: this queue's counter, and the number of tiles it holds (the fetch
@@ -1101,6 +1132,9 @@ struct GemmKernel {
 
       // the previous tile's epilogue buffers (and the published queue position) are free
       lds_barrier();
+      // k-tiles, run in pairs (the stages alternate): an odd count gets one more k-tile past
+      // K, whose loads read zeros and which adds nothing
+      const int nk = (((ti.klen + kBK - 1) / kBK) + 1) & ~1;
       if (nk > 0) {
         if constexpr (kDMA) {
           // k-tiles 0 and 1 -> stages 0 and 1

@@ -1,0 +1,6 @@
+// Instantiations of the persistent GEMM for bf16 operands (every major combination), activation-backward epilogue, varlen-M.
+#include "launch.hpp"
+
+namespace gep {
+template hipError_t launch_family<OP_BF16, true, 1>(const KernelKey&, const KParams&, hipStream_t);
+}  // namespace gep

@@ -1,6 +1,6 @@
-// Instantiations of the persistent GEMM for fp8 operands (K-major; e4m3 / e5m2 mixes), activation-backward epilogue.
+// Instantiations of the persistent GEMM for fp8 operands (K-major, e4m3 or e5m2 in either operand), activation-backward epilogue, dense batched.
 #include "launch.hpp"
 
 namespace gep {
-template hipError_t launch_family<OP_FP8, true>(const KernelKey&, const KParams&, hipStream_t);
+template hipError_t launch_family<OP_FP8, true, 0>(const KernelKey&, const KParams&, hipStream_t);
 }  // namespace gep

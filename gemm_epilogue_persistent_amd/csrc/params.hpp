@@ -28,7 +28,9 @@ struct KParams {
   float alpha, beta;
   const float* alpha_ptr;
   const float* beta_ptr;
-  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens;  // cu_seqlens_m (varlen-M) or cu_seqlens_k (varlen-K)
+  const int32_t* a_idx;       // gathered A rows (varlen-M), or NULL
+  int32_t a_rows;             // rows of A that a_idx may name
   int32_t c_dt, d_dt, p_dt;
   int32_t act;
   // persistent schedule
@@ -59,8 +61,9 @@ struct KernelKey {
   int32_t a_kmajor;  // 1: K contiguous
   int32_t b_kmajor;
   int32_t tile;      // 0: 256x256, 1: 128x128
-  int32_t varlen;
+  int32_t varlen;    // 0 dense, 1 varlen-M, 2 varlen-K
   int32_t dact;      // activation-backward epilogue
+  int32_t gather;    // A rows gathered through a_idx (varlen-M)
 };
 
 }  // namespace gep
@@ -75,7 +78,9 @@ struct gemm_plan {
   int32_t has_c, has_d, has_p;
   int64_t T;          // -1 for varlen
   int32_t max_ctas;
-  int32_t varlen;
+  int32_t varlen;     // varlen-M: T known only on the device
+  int32_t varlen_k;
+  int32_t gather;
   int32_t L;          // groups (varlen) or batches
   int32_t tail_split; // 1: gemm_run may split the last partial round into quarter tiles
 };

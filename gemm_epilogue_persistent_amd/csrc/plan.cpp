@@ -78,6 +78,13 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   if (d.M < 0 || d.N < 0 || d.K < 0 || d.L < 0)
     return fail(GEMM_ERR_INVALID_ARG, "negative size (M=%d N=%d K=%d L=%d)", d.M, d.N, d.K, d.L);
   if (d.varlen_m != 0 && d.varlen_m != 1) return fail(GEMM_ERR_INVALID_ARG, "varlen_m must be 0 or 1");
+  if (d.varlen_k != 0 && d.varlen_k != 1) return fail(GEMM_ERR_INVALID_ARG, "varlen_k must be 0 or 1");
+  if (d.gather_a != 0 && d.gather_a != 1) return fail(GEMM_ERR_INVALID_ARG, "gather_a must be 0 or 1");
+  if (d.varlen_m && d.varlen_k) return fail(GEMM_ERR_INVALID_ARG, "varlen_m and varlen_k are exclusive");
+  if (d.gather_a && !d.varlen_m)
+    return fail(d.varlen_k ? GEMM_ERR_UNSUPPORTED : GEMM_ERR_INVALID_ARG,
+                "gathered A needs varlen-M (gathered A columns for varlen-K are not offered)");
+  if (d.gather_a && d.gather_rows < 0) return fail(GEMM_ERR_INVALID_ARG, "gather_rows < 0");
   const int32_t majors[5] = {d.a_major, d.b_major, d.c_major, d.d_major, d.post_major};
   for (int i = 0; i < 5; ++i)
     if (majors[i] != GEMM_ROW && majors[i] != GEMM_COL)
@@ -107,6 +114,8 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
     if (d.c == DT_NONE) return fail(GEMM_ERR_INVALID_ARG, "dact: C (the pre-activation) is required");
     if (d.d == DT_NONE) return fail(GEMM_ERR_INVALID_ARG, "dact: D (the gradient) is required");
     if (d.beta != 1.0f) return fail(GEMM_ERR_INVALID_ARG, "dact: beta is not used and must be 1");
+    if (d.varlen_k || d.gather_a)
+      return fail(GEMM_ERR_UNSUPPORTED, "dact: not offered with varlen-K or gathered A");
   } else if (d.act != GEMM_ACT_NONE && d.post == DT_NONE) {
     return fail(GEMM_ERR_INVALID_ARG, "an activation needs a PostAct output");
   }
@@ -121,6 +130,8 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   }
   if (d.varlen_m && out_major == GEMM_COL)
     return fail(GEMM_ERR_UNSUPPORTED, "varlen-M needs N-major C/D/PostAct");
+  if (d.gather_a && (es_a != 2 || d.a_major != GEMM_ROW))
+    return fail(GEMM_ERR_UNSUPPORTED, "gathered A must be a 16-bit K-major operand");
 
   // ---- tuning fields
   int32_t G = d.group_m == 0 ? 8 : d.group_m;
@@ -137,12 +148,14 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
 
   // ---- strides and alignment, in the caller's (unswapped) terms
   const int64_t M = d.M, N = d.N, K = d.K;
-  const bool batched = !d.varlen_m && d.L > 1;
+  const bool batched = !d.varlen_m && d.L > 1;  // batched outputs (dense and varlen-K)
+  const bool a_batched = batched && !d.varlen_k;
+  const int64_t rows_a = d.gather_a ? d.gather_rows : M;  // rows A's pointer addresses
   gemm_status st;
-  if (d.a_major == GEMM_ROW) st = check_operand("A", es_a, K, d.lda, M, batched ? d.sa : 0);
-  else st = check_operand("A", es_a, M, d.lda, K, batched ? d.sa : 0);
+  if (d.a_major == GEMM_ROW) st = check_operand("A", es_a, K, d.lda, rows_a, a_batched ? d.sa : 0);
+  else st = check_operand("A", es_a, M, d.lda, K, a_batched ? d.sa : 0);
   if (st != GEMM_OK) return st;
-  const bool b_batched = d.varlen_m ? d.L > 1 : batched;
+  const bool b_batched = d.varlen_m ? d.L > 1 : (batched && !d.varlen_k);
   if (d.b_major == GEMM_ROW) st = check_operand("B", es_b, K, d.ldb, N, b_batched ? d.sb : 0);
   else st = check_operand("B", es_b, N, d.ldb, K, b_batched ? d.sb : 0);
   if (st != GEMM_OK) return st;
@@ -182,22 +195,30 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   k.K = d.K;
   k.L = d.L;
   k.lda = lda; k.ldb = ldb; k.ldc = d.ldc; k.ldd = d.ldd; k.ldp = d.ldp;
-  k.sa = batched ? sa : 0;
-  k.sb = (d.varlen_m ? (d.L > 1) : batched) ? sb : 0;
+  k.sa = a_batched ? sa : 0;
+  k.sb = b_batched ? sb : 0;
   k.sc = batched ? d.sc : 0;
   k.sd = batched ? d.sd : 0;
   k.sp = batched ? d.sp : 0;
   {
     // addressable extents (bytes) of A and B in the kernel's terms; 0 when empty
-    const int64_t rows_a = k.M, rows_b = k.N;
-    const int64_t la = d.varlen_m ? 1 : d.L, lb = d.L;
+    const int64_t ra = swap ? k.M : rows_a, rb = swap ? rows_a : k.N;  // (no swap with gather)
+    const int64_t la = a_batched ? d.L : 1, lb = b_batched ? d.L : 1;
     auto extent = [&](bool kmaj, int64_t rows, int64_t ld, int64_t s, int64_t nb, int es) -> int64_t {
       if (rows == 0 || K == 0 || nb == 0) return 0;
       const int64_t last = kmaj ? (rows - 1) * ld + K : (K - 1) * ld + rows;
       return ((nb - 1) * s + last) * es;
     };
-    k.a_bytes = extent(amaj == GEMM_ROW, rows_a, lda, k.sa, la, es_a);
-    k.b_bytes = extent(bmaj == GEMM_ROW, rows_b, ldb, k.sb, lb, es_b);
+    k.a_bytes = extent(amaj == GEMM_ROW, ra, lda, k.sa, la, es_a);
+    k.b_bytes = extent(bmaj == GEMM_ROW, rb, ldb, k.sb, lb, es_b);
+  }
+  if (d.gather_a) {
+    // gathered rows are addressed from A's base with 32-bit offsets
+    if (k.a_bytes >= ((int64_t)1 << 31) || d.gather_rows >= ((int64_t)1 << 31)) {
+      delete p;
+      return fail(GEMM_ERR_UNSUPPORTED, "gathered A must span less than 2^31 bytes");
+    }
+    k.a_rows = (int32_t)d.gather_rows;
   }
   k.alpha = d.alpha;
   k.beta = d.beta;
@@ -212,8 +233,9 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   key.fmt_b = tb == DT_E5M2 ? 1 : 0;
   key.a_kmajor = amaj == GEMM_ROW ? 1 : 0;
   key.b_kmajor = bmaj == GEMM_ROW ? 1 : 0;
-  key.varlen = d.varlen_m;
+  key.varlen = d.varlen_m ? 1 : (d.varlen_k ? 2 : 0);
   key.dact = d.dact;
+  key.gather = d.gather_a;
 
   // ---- tile choice
   int32_t tmn = 0;
@@ -274,6 +296,8 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   p->tail_split = (d.tail_split != -1 && key.tile == 0) ? 1 : 0;
   p->max_ctas = d.max_ctas;
   p->varlen = d.varlen_m;
+  p->varlen_k = d.varlen_k;
+  p->gather = d.gather_a;
   p->L = d.L;
   p->has_c = d.c != DT_NONE;
   p->has_d = d.d != DT_NONE;

@@ -14,7 +14,11 @@
  *   - page 5, GemmSm90.__call__ and kernel: the varlen-M (grouped) mode, where cu_seqlens_m
  *     splits the rows of A / C / D into groups and group g multiplies by its own B[g];
  *   - page 5, GemmSm90.is_valid_dtypes: fp16 / bf16 / e4m3 / e5m2 inputs, fp32 accumulation,
- *     fp8 operands K-major only.
+ *     fp8 operands K-major only;
+ *   - page 5, GemmSm90.kernel, and the torch-vendored quack/gemm_sm90.py page: the varlen-K
+ *     (grouped K) mode, where cu_seqlens_k splits the K range of A and B into groups that
+ *     each produce one output batch, and gathered A (mAIdx: A rows read through an index
+ *     array).
  * SiLU is an addition of this library (x * sigmoid(x)).
  *
  * Conventions used by every entry point:
@@ -96,6 +100,23 @@ typedef enum {
  * C, D and PostAct that are present must share one major mode.
  * Varlen mode supports only GEMM_ROW outputs.
  *
+ * Varlen-K mode (varlen_k == 1; page 5, GemmSm90.kernel offsets A and B along K by
+ * cu_seqlens_k[l] and ends the group's K range at cu_seqlens_k[l+1]): L is the number of
+ * groups and K the total K extent of A and B. A is (M, K) and B is (N, K) with no batch
+ * index (sa, sb ignored); C/D/PostAct are (L, M, N) with batch strides sc/sd/sp, batch l
+ * holding group l: D[l] = alpha * A[:, k in group l] x B[:, k in group l]^T (+ beta C[l]),
+ * an empty group giving alpha * 0. cu_seqlens_k (device int32[L+1], in gemm_args) gives
+ * the ranges; precondition (not checked): cu[0] == 0, non-decreasing, cu[L] <= K, and when
+ * A or B is K-major, every cu[g] times the element size a multiple of 16 bytes (the group
+ * starts on a 16-byte chunk). Any major modes and output majors; no activation backward.
+ * varlen_m and varlen_k are exclusive.
+ *
+ * Gathered A (gather_a == 1, varlen-M plans only; the pages' mAIdx and
+ * load_AB_gather_A): output row r (global, in [0, M)) reads A row a_idx[r] instead of row r.
+ * A is then (gather_rows, K), K-major, 16-bit, at most 2^31 bytes from its pointer; a_idx
+ * (device int32[M], in gemm_args) may repeat rows; an index outside [0, gather_rows) reads
+ * zeros. No activation backward. (Gathered A columns for varlen-K are not offered.)
+ *
  * Activation backward (dact = 1; page 6, quack/gemm_dact_sm90.py, GemmDActSm90): the product
  * is the incoming gradient dout = alpha * A x B, C holds the saved pre-activation x (its
  * own type), and the outputs are D = dout * act'(x) (required) and PostAct = act(x)
@@ -144,7 +165,26 @@ typedef struct {
   int32_t tail_split;
   int32_t raster_order;
   int32_t dact;     /* 1: activation-backward epilogue (see above) */
+  int32_t varlen_k; /* 0 or 1: grouped K (see above) */
+  int32_t gather_a; /* 0 or 1: A rows gathered through a_idx (varlen-M) */
+  int64_t gather_rows; /* gather_a: rows of A that a_idx may name */
 } gemm_desc;
+
+/* Run-time arguments of gemm_run_ex (all device pointers, owned by the caller; NULL where
+ * the plan does not use them). */
+typedef struct {
+  const void* A;
+  const void* B;
+  const void* C;
+  void* D;
+  void* PostAct;
+  const float* alpha_dev;        /* optional device fp32, replaces desc.alpha            */
+  const float* beta_dev;         /* optional device fp32, replaces desc.beta             */
+  const int32_t* cu_seqlens_m;   /* varlen-M plans: int32[L+1]                           */
+  const int32_t* cu_seqlens_k;   /* varlen-K plans: int32[L+1]                           */
+  const int32_t* a_idx;          /* gather_a plans: int32[M]                             */
+  int32_t* tile_counters;        /* NULL: static schedule; else as in gemm_run_dynamic  */
+} gemm_args;
 
 typedef struct gemm_plan gemm_plan;
 
@@ -183,6 +223,16 @@ gemm_status gemm_run_logged(const gemm_plan* plan, const void* A, const void* B,
                             void* D, void* PostAct, const float* alpha_dev, const float* beta_dev,
                             const int32_t* cu_seqlens_m, int32_t* tile_log, int32_t max_iters,
                             void* stream);
+
+/* The general entry point: every plan, including varlen-K and gathered-A plans, which
+ * gemm_run, gemm_run_logged and gemm_run_dynamic reject with INVALID_ARG. The fields of
+ * `args` mean what the same-named arguments of gemm_run mean; cu_seqlens_k and a_idx are
+ * required iff the plan has varlen_k / gather_a, and a device array the plan does not use
+ * must be NULL (INVALID_ARG otherwise). tile_counters non-NULL selects the dynamic schedule
+ * exactly as gemm_run_dynamic (its counters must be zero before the first call and are left
+ * zero). Asynchronous on `stream`; ALIGNMENT for operand pointers not 16-byte aligned or
+ * index arrays not 4-byte aligned, HIP if a launch fails. */
+gemm_status gemm_run_ex(const gemm_plan* plan, const gemm_args* args, void* stream);
 
 /* As gemm_run (or, with tile_log non-NULL, gemm_run_logged), with the dynamic persistent
  * schedule: the page 5 GEMM's optional tile_count_semaphore, a device counter from which

@@ -40,13 +40,15 @@ def run_hip(inp, d_major_m=False, tile=None, alpha_dev=None, beta_dev=None, tile
     D = out_like(inp, inp.d_dt, d_major_m) if inp.d_dt != "none" else None
     P = out_like(inp, inp.post_dt, d_major_m) if inp.post_dt != "none" else None
     cu = torch.from_numpy(inp.cu_seqlens).to("cuda") if inp.varlen else None
+    cuk = torch.from_numpy(inp.cu_seqlens_k).to("cuda") if inp.cu_seqlens_k is not None else None
+    idx = torch.from_numpy(inp.a_idx).to("cuda") if inp.a_idx is not None else None
     if tile is not None:
         tuning["tile"] = tile
     if inp.dact:
         tuning["dact"] = True
-    plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu, **tuning)
+    plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, cu, cuk, idx, **tuning)
     plan.run(A, B, C, D, P, alpha_dev, beta_dev, cu, tile_log=tile_log, max_iters=max_iters,
-             tile_counters=tile_counters)
+             tile_counters=tile_counters, cu_seqlens_k=cuk, a_idx=idx)
     torch.cuda.synchronize()
     d = None if D is None else D.double().cpu().numpy()
     p = None if P is None else P.double().cpu().numpy()

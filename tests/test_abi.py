@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"gemm_create", "gemm_run", "gemm_destroy", "gemm_run_logged", "gemm_run_dynamic", "gemm_plan_grid",
+    assert {"gemm_create", "gemm_run", "gemm_run_ex", "gemm_destroy", "gemm_run_logged", "gemm_run_dynamic",
+            "gemm_plan_grid",
             "gemm_fastdivmod_params", "gemm_fastdivmod_check", "gemm_status_string",
             "gemm_last_error"} <= names
     for n in names:
@@ -72,6 +73,14 @@ def test_create_accepts_valid(lib):
     assert create(lib, d) == _abi.OK
     d = base_desc(c=_abi.DT["f32"], ldc=256, post=_abi.DT["bf16"], ldp=256, act=_abi.ACT["gelu_tanh"])
     assert create(lib, d) == _abi.OK
+    # varlen-K: A (M, K) M-major, B (N, K) N-major, D (L, M, N); M-major D as well
+    d = base_desc(varlen_k=1, L=4, a_major=_abi.COL, b_major=_abi.COL, sd=65536)
+    assert create(lib, d) == _abi.OK
+    assert create(lib, base_desc(varlen_k=1, L=4, sd=65536, d_major=_abi.COL)) == _abi.OK
+    assert create(lib, base_desc(varlen_k=1, L=3, a=_abi.DT["e4m3"], b=_abi.DT["e5m2"], sd=65536)) == _abi.OK
+    # gathered A rows: A (gather_rows, K) K-major
+    assert create(lib, base_desc(varlen_m=1, L=2, sb=65536, gather_a=1, gather_rows=1000)) == _abi.OK
+    assert create(lib, base_desc(varlen_m=1, L=2, sb=65536, gather_a=1, gather_rows=10, b_major=_abi.COL)) == _abi.OK
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -108,6 +117,17 @@ def test_create_accepts_valid(lib):
     (dict(varlen_m=1, L=2, sb=65536, d_major=_abi.COL), _abi.UNSUPPORTED),
     (dict(L=2, sa=65536, sb=65536, sd=65536 + 4), _abi.ALIGNMENT),
     (dict(L=2, sa=65536, sb=65536, sd=65536 - 256), _abi.INVALID_ARG),  # D batches overlap
+    (dict(varlen_k=2), _abi.INVALID_ARG),
+    (dict(varlen_k=1, varlen_m=1, L=2, sb=65536), _abi.INVALID_ARG),  # exclusive modes
+    (dict(varlen_k=1, L=2, sd=65536, dact=1, c=2, ldc=256, sc=65536), _abi.UNSUPPORTED),
+    (dict(gather_a=1, gather_rows=10), _abi.INVALID_ARG),  # gather without varlen
+    (dict(gather_a=1, gather_rows=10, varlen_k=1, L=2, sd=65536), _abi.UNSUPPORTED),  # gathered columns
+    (dict(gather_a=2, varlen_m=1, L=2, sb=65536), _abi.INVALID_ARG),
+    (dict(gather_a=1, gather_rows=-1, varlen_m=1, L=2, sb=65536), _abi.INVALID_ARG),
+    (dict(gather_a=1, gather_rows=10, varlen_m=1, L=2, sb=65536, a_major=_abi.COL), _abi.UNSUPPORTED),
+    (dict(gather_a=1, gather_rows=10, varlen_m=1, L=2, sb=65536, a=4, b=4), _abi.UNSUPPORTED),  # fp8
+    (dict(gather_a=1, gather_rows=1 << 23, varlen_m=1, L=2, sb=65536), _abi.UNSUPPORTED),  # >= 2^31 bytes
+    (dict(gather_a=1, gather_rows=10, varlen_m=1, L=2, sb=65536, dact=1, c=2, ldc=256), _abi.UNSUPPORTED),
 ])
 def test_create_rejects(lib, kw, status):
     assert create(lib, base_desc(**kw)) == status

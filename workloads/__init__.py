@@ -8,9 +8,11 @@ slot A = 0, B = 1, C = 2, group sizes = 3.
 
 Every generator returns an `Inputs` with CPU tensors:
   store_*   the contiguous storage tensor in the operand type;
-  A, B, C   logical views: A (L, M, K), B (L, N, K), C (L, M, N) (varlen: A (M, K),
-            B (G, N, K), C (M, N)); an M-major A is a permuted view of a [L][K][M] store.
-plus the scalars of the problem (alpha, beta, activation, cu_seqlens_m, output types).
+  A, B, C   logical views: A (L, M, K), B (L, N, K), C (L, M, N) (varlen-M: A (M, K) or,
+            gathered, (rows, K), B (G, N, K), C (M, N); varlen-K: A (M, K), B (N, K),
+            C (G, M, N)); an M-major A is a permuted view of a [L][K][M] store.
+plus the scalars of the problem (alpha, beta, activation, cu_seqlens_m / cu_seqlens_k,
+the gather index a_idx, output types).
 """
 from dataclasses import dataclass, field
 from typing import Optional
@@ -46,6 +48,8 @@ class Inputs:
     cu_seqlens: Optional[np.ndarray] = None
     dact: bool = False  # activation backward: C is the pre-activation, D = (alpha A x B) * act'(C)
     extra: dict = field(default_factory=dict)
+    cu_seqlens_k: Optional[np.ndarray] = None  # varlen-K: K ranges of the G groups (K = total extent)
+    a_idx: Optional[np.ndarray] = None         # gathered A: the A row of each global output row
 
     @property
     def varlen(self) -> bool:
@@ -54,6 +58,8 @@ class Inputs:
     def flops(self) -> float:
         if self.varlen:
             return 2.0 * self.M * self.N * self.K
+        if self.cu_seqlens_k is not None:
+            return 2.0 * self.M * self.N * float(self.cu_seqlens_k[-1])
         return 2.0 * self.M * self.N * self.K * self.L
 
 
@@ -217,6 +223,39 @@ def varlen_moe(G=8, N=4096, K=4096, sizes=None, std=1.0 / 64.0, act="silu"):
                   post_dt="bf16", act=act, cu_seqlens=cu)
 
 
+def varlen_k_moe(G=8, M=4096, N=4096, sizes=None, std=1.0, k_unit=128):
+    """Varlen-K (grouped K, the weight gradient of a grouped MoE layer): G groups of
+    K_g = 128 * U{1..32} tokens (the group-size law of the varlen-M workload), A = X^T with X
+    (sum K_g, M) bf16 row-major, i.e. A (M, K) M-major; B = dY^T with dY (sum K_g, N) bf16
+    row-major, i.e. B (N, K) N-major; A, B ~ N(0,1) * std; D (G, M, N) bf16."""
+    s = 1111 + 10 * 6
+    if sizes is None:
+        sizes = group_sizes(s + 3, G, unit=k_unit)
+    sizes = np.asarray(sizes, dtype=np.int64)
+    cu = np.zeros(len(sizes) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(sizes)
+    K = int(cu[-1])
+    A = normal(s + 0, (K, M), "bf16", std).t()
+    B = normal(s + 1, (K, N), "bf16", std).t()
+    return Inputs(f"varlen_k_{len(sizes)}x{M}x{N}_bf16", M, N, K, len(sizes), "bf16", "bf16", A, B,
+                  d_dt="bf16", cu_seqlens_k=cu)
+
+
+def varlen_moe_gather(G=8, N=4096, K=4096, sizes=None, std=1.0 / 64.0, act="silu", topk=2):
+    """The varlen-M workload with gathered A (MoE tokens read through the routing index):
+    X has sum(M_g) / topk token rows ~ N(0,1)/64 and a_idx names, for every row of the
+    expert-sorted problem, the token it reads (seeded, uniform over the tokens)."""
+    s = 1111 + 10 * 7
+    inp = varlen_moe(G, N, K, sizes, std, act)
+    rows = max(1, inp.M // topk)
+    X = normal(s + 0, (rows, K), "bf16", std)
+    a_idx = rng(s + 4).integers(0, rows, size=inp.M).astype(np.int32)
+    inp.name = f"varlen_m_gather_{G}x{N}x{K}_bf16_silu"
+    inp.A = X
+    inp.a_idx = a_idx
+    return inp
+
+
 WORKLOADS = {
     "plain_256": plain_256,
     "act_4096": act_4096,
@@ -226,6 +265,8 @@ WORKLOADS = {
     "fp8_8192": fp8_8192,
     "varlen_moe": varlen_moe,
     "dact_4096": dact_4096,
+    "varlen_k_moe": varlen_k_moe,
+    "varlen_moe_gather": varlen_moe_gather,
 }
 
 
