@@ -113,9 +113,17 @@ __device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mswz(int k) { return (k & 3) << 2; }
 
 // Buffer resource over [base, base + bytes); reads at offsets >= bytes return zero.
+// The base and extent are the same in every lane (they depend on the tile only); reading
+// them through readfirstlane states that, so the descriptor stays in SGPRs. (Where the
+// compiler cannot tell and has moved them to VGPRs, it otherwise wraps every buffer
+// instruction in a loop over the distinct descriptor values.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
 // Loader of one operand's k-tile: ROWS rows (M or N) by kRowBytes of K, staged through
