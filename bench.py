@@ -24,7 +24,7 @@ PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "e4m3": 5000.0, "e5m2": 5000.0}
 HBM_PEAK_GBS = 8000.0
 PRIMARY = "square_8192_bf16"
 SECONDARY = ["fp8_8192", "varlen_moe", "square_8192_f16", "act_4096", "batched_2048", "dact_4096",
-             "varlen_k_moe", "varlen_moe_gather"]
+             "varlen_k_moe", "varlen_moe_gather", "varlen_k_moe_gather"]
 
 
 def source_hash():
@@ -45,7 +45,7 @@ def algorithmic_bytes(inp):
         b = inp.L * inp.N * inp.K * es[inp.b_dt]
         mn = inp.M * inp.N
     elif inp.cu_seqlens_k is not None:
-        a = inp.M * inp.K * es[inp.a_dt]
+        a = inp.M * (inp.A.shape[1] if inp.a_idx is not None else inp.K) * es[inp.a_dt]
         b = inp.N * inp.K * es[inp.b_dt]
         mn = inp.L * inp.M * inp.N
     else:

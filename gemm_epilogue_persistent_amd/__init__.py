@@ -13,7 +13,8 @@ with the major mode of each read from its strides; 2-D tensors mean l = 1. In va
 mode (cu_seqlens_m given) A is (M, K), B is (G, N, K), C / D / PostAct are (M, N); with
 a_idx (gathered A) A is (rows, K) and output row r reads A row a_idx[r]. In varlen-K mode
 (cu_seqlens_k given; the same pages' grouped K) A is (M, K), B is (N, K) and C / D /
-PostAct are (G, M, N), group g summing k over [cu_seqlens_k[g], cu_seqlens_k[g+1]).
+PostAct are (G, M, N), group g summing k over [cu_seqlens_k[g], cu_seqlens_k[g+1]); with
+a_idx, A is M-major (M, cols) and global k reads A column a_idx[k].
 """
 import ctypes
 
@@ -71,6 +72,8 @@ def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none"
     if varlen_k:
         M, K = A.shape
         N, K2 = B.shape
+        if gather:  # gathered k-rows: A's K extent is its own; the groups index B's K
+            K = K2
         L = varlen_k
         A3, B3 = A.unsqueeze(0), B.unsqueeze(0)
         C3, D3, P3 = (_as3(x) for x in (C, D, PostAct))
@@ -118,7 +121,7 @@ def describe(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none"
     d.dact = 1 if dact else 0
     d.varlen_k = 1 if varlen_k else 0
     d.gather_a = 1 if gather else 0
-    d.gather_rows = A.shape[0] if gather else 0
+    d.gather_rows = (A.shape[1] if varlen_k else A.shape[0]) if gather else 0
     return d
 
 

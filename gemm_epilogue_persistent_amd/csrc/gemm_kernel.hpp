@@ -194,6 +194,38 @@ struct TileLoader {
     else klim = K - (((lane % kChunks) ^ kswz(wave * (1024 / kRowBytes) + lane / kChunks)) * (16 / ES));
   }
 
+  // M/N-major operand with gathered k-rows: k-row k of the group reads operand row
+  // kidx[k]. The row of each chunk changes with the k-tile, so the loader keeps the index of
+  // its chunks' rows for the k-tile it loads next (gidx, fetched one k-tile ahead) and
+  // only the column offset (coff) of each chunk.
+  int32_t gidx[kInstr];
+  uint32_t coff[kInstr];
+  int32_t krow0;  // k-row of chunk 0 inside a k-tile; chunk q is krow0 + q * kDK
+  __device__ __forceinline__ void init_gather_k(int wave, int lane, int rows_valid, int K) {
+    static_assert(!KMAJ, "gathered k-rows need an M/N-major operand");
+    krow0 = wave * kKPI + lane / kCPR;
+#pragma unroll
+    for (int q = 0; q < kInstr; ++q) {
+      const int krow = q * kDK + krow0;
+      const int c = (lane % kCPR) ^ mswz(krow);
+      coff[q] = c * (16 / ES) < rows_valid ? (uint32_t)(c * 16) : kOOB;
+    }
+    klim = K - krow0;
+  }
+  // Operand row indices of chunk Q's k-row in the k-tile at k0 (reads past the group's
+  // index range return 0; those chunks are not loaded).
+  template <int Q>
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t irs, int k0) {
+    gidx[Q] = __builtin_amdgcn_raw_buffer_load_b32(irs, (k0 + krow0 + Q * kDK) * 4, 0, 0);
+  }
+  // Global -> registers, chunk Q of the k-tile at k0 whose rows gidx holds; `rows` bounds
+  // the operand rows an index may name (others read as zero).
+  template <int Q>
+  __device__ __forceinline__ void load_gather(__amdgpu_buffer_rsrc_t rs, int k0, uint32_t ld_bytes, uint32_t rows) {
+    const bool ok = k0 + Q * kDK < klim && coff[Q] != kOOB && (uint32_t)gidx[Q] < rows;
+    reg[Q] = __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? (uint32_t)gidx[Q] * ld_bytes + coff[Q] : kOOB, 0, 0);
+  }
+
   // Global -> registers, chunk Q of the k-tile starting at element k0 of K. Chunks at
   // k >= K (the K tail, and whole k-tiles past the end) read as zero.
   template <int Q>
@@ -424,6 +456,7 @@ __device__ __forceinline__ void raster(const KParams& p, uint32_t r, uint32_t ta
 struct TileInfo {
   int l, m0, n0, row_end;
   int klen;            // K extent of the tile's problem (varlen-K: of its group)
+  int kb;              // varlen-K: the group's first k
   int mb, nb;          // block coordinates inside the batch / group
   const char* a_tile;  // first byte of the tile's A rows (K-major) / columns (M-major)
   const char* b_tile;
@@ -438,7 +471,8 @@ template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, int VM, in
 struct GemmKernel {
   static constexpr bool VARLEN = VM == 1;
   static constexpr bool VARK = VM == 2;
-  static_assert(!GA || (VARLEN && A_K), "gathered A rows: varlen-M with a K-major A");
+  static_assert(!GA || (VARLEN && A_K) || (VARK && !A_K), "gathered A: rows of a K-major A (varlen-M) or k-rows of an M-major A (varlen-K)");
+  static constexpr bool GAK = GA && VARK;  // gathered k-rows of A
   // NW wave64s in a 2 x (NW/2) grid over the output tile
   static constexpr int kThreads = NW * 64;
   using Op = Mfma<OP, FA, FB>;
@@ -570,9 +604,13 @@ struct GemmKernel {
     }
     const int64_t a_lb = (VARLEN || VARK) ? 0 : (int64_t)ti.l * p.sa;
     const int64_t b_lb = VARK ? 0 : (int64_t)ti.l * p.sb;
-    // gathered A: the loader's offsets count from A's base (rows come from a_idx)
+    // gathered A: the loader's offsets count from A's base (rows come from a_idx), or for
+    // gathered k-rows from the tile's first column
+    ti.kb = (int)kb;
     const int64_t a_off =
-        GA ? 0 : (a_lb + (A_K ? (int64_t)ti.m0 * p.lda + kb : kb * p.lda + (int64_t)ti.m0)) * kES;
+        (GA && VARLEN) ? 0
+                       : (GAK ? (int64_t)ti.m0 * kES
+                              : (a_lb + (A_K ? (int64_t)ti.m0 * p.lda + kb : kb * p.lda + (int64_t)ti.m0)) * kES);
     const int64_t b_off = (b_lb + (B_K ? (int64_t)ti.n0 * p.ldb + kb : kb * p.ldb + (int64_t)ti.n0)) * kES;
     ti.a_tile = (const char*)p.A + a_off;
     ti.b_tile = (const char*)p.B + b_off;
@@ -585,12 +623,26 @@ struct GemmKernel {
   struct KtSrc {
     __amdgpu_buffer_rsrc_t a, b;
     int k0;
+    // gathered k-rows only: the group's index range, A's leading dimension in bytes and the
+    // number of rows of A an index may name
+    __amdgpu_buffer_rsrc_t ia;
+    uint32_t ld, rows;
   };
   static __device__ __forceinline__ KtSrc kt_src(const KParams& p, const TileInfo& ti, int j) {
-    const int64_t a_step = A_K ? (int64_t)kRowBytes : (int64_t)kBK * p.lda * kES;
+    // (gathered k-rows: one resource for all k-tiles, the rows come from the index)
+    const int64_t a_step = GAK ? 0 : (A_K ? (int64_t)kRowBytes : (int64_t)kBK * p.lda * kES);
     const int64_t b_step = B_K ? (int64_t)kRowBytes : (int64_t)kBK * p.ldb * kES;
     const int64_t ao = (int64_t)j * a_step, bo = (int64_t)j * b_step;
-    return KtSrc{make_rsrc(ti.a_tile + ao, ti.a_room - ao), make_rsrc(ti.b_tile + bo, ti.b_room - bo), j * kBK};
+    KtSrc r;
+    r.a = make_rsrc(ti.a_tile + ao, ti.a_room - ao);
+    r.b = make_rsrc(ti.b_tile + bo, ti.b_room - bo);
+    r.k0 = j * kBK;
+    if constexpr (GAK) {
+      r.ia = make_rsrc(p.a_idx + ti.kb, (int64_t)ti.klen * 4);
+      r.ld = (uint32_t)(p.lda * kES);
+      r.rows = (uint32_t)p.a_rows;
+    }
+    return r;
   }
 
   // Register chunk C (A chunks first, then B): write it to the LDS stage `wr`, then reload it
@@ -600,7 +652,12 @@ struct GemmKernel {
                                                      int lane) {
     if constexpr (C < LA::kInstr) {
       la.template store<C>(wr, wave, lane);
-      la.template load<C>(src.a, src.k0);
+      if constexpr (GAK) {
+        la.template load_gather<C>(src.a, src.k0, src.ld, src.rows);
+        la.template fetch<C>(src.ia, src.k0 + kBK);
+      } else {
+        la.template load<C>(src.a, src.k0);
+      }
     } else {
       lb.template store<C - LA::kInstr>(wr + kBOff, wave, lane);
       lb.template load<C - LA::kInstr>(src.b, src.k0);
@@ -614,12 +671,29 @@ struct GemmKernel {
       cycle_chunks<C0 + 1, N - 1>(la, lb, wr, src, wave, lane);
     }
   }
+  // Gathered k-rows: the row indices of a tile's k-tile 0.
+  template <int C = 0>
+  static __device__ __forceinline__ void fetch_all(LA& la, __amdgpu_buffer_rsrc_t irs) {
+    if constexpr (C < LA::kInstr) {
+      la.template fetch<C>(irs, 0);
+      fetch_all<C + 1>(la, irs);
+    }
+  }
+
   // Only the loads (the tile's first k-tile).
   template <int C = 0>
   static __device__ __forceinline__ void load_all(LA& la, LB& lb, const KtSrc& src) {
     if constexpr (C < kChunksPerKt) {
-      if constexpr (C < LA::kInstr) la.template load<C>(src.a, src.k0);
-      else lb.template load<C - LA::kInstr>(src.b, src.k0);
+      if constexpr (C < LA::kInstr) {
+        if constexpr (GAK) {
+          la.template load_gather<C>(src.a, src.k0, src.ld, src.rows);
+          la.template fetch<C>(src.ia, src.k0 + kBK);
+        } else {
+          la.template load<C>(src.a, src.k0);
+        }
+      } else {
+        lb.template load<C - LA::kInstr>(src.b, src.k0);
+      }
       load_all<C + 1>(la, lb, src);
     }
   }
@@ -1131,10 +1205,18 @@ struct GemmKernel {
     // a tile's first k-tile goes into the staging registers as early as possible
     auto begin_tile = [&](int t) {
       ti = decode(p, t, gstart, t_lo);
-      if constexpr (GA) la.init_gather(wave, lane, ti.row_end - ti.m0, p.lda * kES, ti.klen, p.a_idx + ti.m0, p.a_rows);
+      if constexpr (GAK) la.init_gather_k(wave, lane, ti.row_end - ti.m0, ti.klen);
+      else if constexpr (GA) la.init_gather(wave, lane, ti.row_end - ti.m0, p.lda * kES, ti.klen, p.a_idx + ti.m0, p.a_rows);
       else la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES, ti.klen);
       lb.init(wave, lane, p.N - ti.n0, p.ldb * kES, ti.klen);
-      if constexpr (!kDMA) load_all(la, lb, kt_src(p, ti, 0));
+      if constexpr (GAK) {
+        static_assert(!kDMA, "gathered k-rows go through the staging registers");
+        const KtSrc s0 = kt_src(p, ti, 0);
+        fetch_all(la, s0.ia);
+        load_all(la, lb, s0);
+      } else if constexpr (!kDMA) {
+        load_all(la, lb, kt_src(p, ti, 0));
+      }
     };
     // dynamic schedule: this queue's counter, and the number of tiles it holds (the fetch
     // that returns the last value returns the counter to zero for the next launch)

@@ -20,8 +20,8 @@ template <int BM, int OP, bool AK, bool BK>
 constexpr int waves() { return (BM == 256 && OP != OP_FP8 && AK && BK) ? 8 : 4; }
 
 // VM: 0 dense batched, 1 varlen-M, 2 varlen-K. DA: the activation-backward epilogue (its own
-// instantiations, so that the forward kernels carry none of its code or registers). GA: A rows
-// gathered through a_idx (varlen-M, K-major A).
+// instantiations, so that the forward kernels carry none of its code or registers). GA: A read
+// through a_idx: its rows (varlen-M, K-major A) or its k-rows (varlen-K, M-major A).
 template <int BM, int OP, int FA, int FB, bool AK, bool BK, int VM, bool DA, bool GA>
 __global__ __launch_bounds__((waves<BM, OP, AK, BK>() * 64), (wg_per_cu<BM>())) void gemm_persistent_kernel(
     const KParams p) {
@@ -51,10 +51,15 @@ hipError_t by_layout(const KernelKey& k, const KParams& p, hipStream_t s) {
     return launch_one<BM, OP, 1, 1, true, true, VM, DA, false>(p, s);
   } else {
     if (k.gather) {
-      if constexpr (VM == 1 && !DA) {
+      if constexpr (VM == 1 && !DA) {  // gathered rows of a K-major A
         if (!k.a_kmajor) return hipErrorInvalidValue;
         if (k.b_kmajor) return launch_one<BM, OP, 0, 0, true, true, VM, DA, true>(p, s);
         return launch_one<BM, OP, 0, 0, true, false, VM, DA, true>(p, s);
+      }
+      if constexpr (VM == 2 && !DA) {  // gathered k-rows of an M-major A
+        if (k.a_kmajor) return hipErrorInvalidValue;
+        if (k.b_kmajor) return launch_one<BM, OP, 0, 0, false, true, VM, DA, true>(p, s);
+        return launch_one<BM, OP, 0, 0, false, false, VM, DA, true>(p, s);
       }
       return hipErrorInvalidValue;
     }

@@ -81,9 +81,8 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   if (d.varlen_k != 0 && d.varlen_k != 1) return fail(GEMM_ERR_INVALID_ARG, "varlen_k must be 0 or 1");
   if (d.gather_a != 0 && d.gather_a != 1) return fail(GEMM_ERR_INVALID_ARG, "gather_a must be 0 or 1");
   if (d.varlen_m && d.varlen_k) return fail(GEMM_ERR_INVALID_ARG, "varlen_m and varlen_k are exclusive");
-  if (d.gather_a && !d.varlen_m)
-    return fail(d.varlen_k ? GEMM_ERR_UNSUPPORTED : GEMM_ERR_INVALID_ARG,
-                "gathered A needs varlen-M (gathered A columns for varlen-K are not offered)");
+  if (d.gather_a && !d.varlen_m && !d.varlen_k)
+    return fail(GEMM_ERR_INVALID_ARG, "gathered A needs varlen-M or varlen-K");
   if (d.gather_a && d.gather_rows < 0) return fail(GEMM_ERR_INVALID_ARG, "gather_rows < 0");
   const int32_t majors[5] = {d.a_major, d.b_major, d.c_major, d.d_major, d.post_major};
   for (int i = 0; i < 5; ++i)
@@ -130,8 +129,11 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   }
   if (d.varlen_m && out_major == GEMM_COL)
     return fail(GEMM_ERR_UNSUPPORTED, "varlen-M needs N-major C/D/PostAct");
-  if (d.gather_a && (es_a != 2 || d.a_major != GEMM_ROW))
-    return fail(GEMM_ERR_UNSUPPORTED, "gathered A must be a 16-bit K-major operand");
+  if (d.gather_a && d.varlen_m && (es_a != 2 || d.a_major != GEMM_ROW))
+    return fail(GEMM_ERR_UNSUPPORTED, "gathered A rows (varlen-M): A must be a 16-bit K-major operand");
+  if (d.gather_a && d.varlen_k && (es_a != 2 || d.a_major != GEMM_COL || out_major == GEMM_COL))
+    return fail(GEMM_ERR_UNSUPPORTED,
+                "gathered A columns (varlen-K): A must be a 16-bit M-major operand and the outputs N-major");
 
   // ---- tuning fields
   int32_t G = d.group_m == 0 ? 8 : d.group_m;
@@ -150,10 +152,11 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   const int64_t M = d.M, N = d.N, K = d.K;
   const bool batched = !d.varlen_m && d.L > 1;  // batched outputs (dense and varlen-K)
   const bool a_batched = batched && !d.varlen_k;
-  const int64_t rows_a = d.gather_a ? d.gather_rows : M;  // rows A's pointer addresses
+  const int64_t rows_a = (d.gather_a && d.varlen_m) ? d.gather_rows : M;  // rows A's pointer addresses
+  const int64_t cols_a = (d.gather_a && d.varlen_k) ? d.gather_rows : K;  // its K extent
   gemm_status st;
   if (d.a_major == GEMM_ROW) st = check_operand("A", es_a, K, d.lda, rows_a, a_batched ? d.sa : 0);
-  else st = check_operand("A", es_a, M, d.lda, K, a_batched ? d.sa : 0);
+  else st = check_operand("A", es_a, M, d.lda, cols_a, a_batched ? d.sa : 0);
   if (st != GEMM_OK) return st;
   const bool b_batched = d.varlen_m ? d.L > 1 : (batched && !d.varlen_k);
   if (d.b_major == GEMM_ROW) st = check_operand("B", es_b, K, d.ldb, N, b_batched ? d.sb : 0);
@@ -204,13 +207,13 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
     // addressable extents (bytes) of A and B in the kernel's terms; 0 when empty
     const int64_t ra = swap ? k.M : rows_a, rb = swap ? rows_a : k.N;  // (no swap with gather)
     const int64_t la = a_batched ? d.L : 1, lb = b_batched ? d.L : 1;
-    auto extent = [&](bool kmaj, int64_t rows, int64_t ld, int64_t s, int64_t nb, int es) -> int64_t {
-      if (rows == 0 || K == 0 || nb == 0) return 0;
-      const int64_t last = kmaj ? (rows - 1) * ld + K : (K - 1) * ld + rows;
+    auto extent = [&](bool kmaj, int64_t rows, int64_t ld, int64_t s, int64_t nb, int es, int64_t kx) -> int64_t {
+      if (rows == 0 || kx == 0 || nb == 0) return 0;
+      const int64_t last = kmaj ? (rows - 1) * ld + kx : (kx - 1) * ld + rows;
       return ((nb - 1) * s + last) * es;
     };
-    k.a_bytes = extent(amaj == GEMM_ROW, ra, lda, k.sa, la, es_a);
-    k.b_bytes = extent(bmaj == GEMM_ROW, rb, ldb, k.sb, lb, es_b);
+    k.a_bytes = extent(amaj == GEMM_ROW, ra, lda, k.sa, la, es_a, cols_a);
+    k.b_bytes = extent(bmaj == GEMM_ROW, rb, ldb, k.sb, lb, es_b, K);
   }
   if (d.gather_a) {
     // gathered rows are addressed from A's base with 32-bit offsets

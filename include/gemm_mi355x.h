@@ -111,11 +111,14 @@ typedef enum {
  * starts on a 16-byte chunk). Any major modes and output majors; no activation backward.
  * varlen_m and varlen_k are exclusive.
  *
- * Gathered A (gather_a == 1, varlen-M plans only; the pages' mAIdx and
- * load_AB_gather_A): output row r (global, in [0, M)) reads A row a_idx[r] instead of row r.
- * A is then (gather_rows, K), K-major, 16-bit, at most 2^31 bytes from its pointer; a_idx
- * (device int32[M], in gemm_args) may repeat rows; an index outside [0, gather_rows) reads
- * zeros. No activation backward. (Gathered A columns for varlen-K are not offered.)
+ * Gathered A (gather_a == 1; the pages' mAIdx, load_AB_gather_A and the torch-vendored
+ * page's gather copies), 16-bit A at most 2^31 bytes from its pointer, no activation backward:
+ *   - varlen-M: output row r (global, in [0, M)) reads A row a_idx[r] instead of row r. A is
+ *     (gather_rows, K), K-major; a_idx is device int32[M].
+ *   - varlen-K: global k (in [0, K)) reads A column a_idx[k] instead of column k. A is
+ *     (M, gather_rows), M-major (each column one contiguous row of storage); a_idx is device
+ *     int32[K]; C/D/PostAct N-major. B is not gathered.
+ * a_idx (in gemm_args) may repeat indices; an index outside [0, gather_rows) reads zeros.
  *
  * Activation backward (dact = 1; page 6, quack/gemm_dact_sm90.py, GemmDActSm90): the product
  * is the incoming gradient dout = alpha * A x B, C holds the saved pre-activation x (its
@@ -167,7 +170,7 @@ typedef struct {
   int32_t dact;     /* 1: activation-backward epilogue (see above) */
   int32_t varlen_k; /* 0 or 1: grouped K (see above) */
   int32_t gather_a; /* 0 or 1: A rows gathered through a_idx (varlen-M) */
-  int64_t gather_rows; /* gather_a: rows of A that a_idx may name */
+  int64_t gather_rows; /* gather_a: rows (varlen-M) or columns (varlen-K) of A that a_idx may name */
 } gemm_desc;
 
 /* Run-time arguments of gemm_run_ex (all device pointers, owned by the caller; NULL where
@@ -182,7 +185,7 @@ typedef struct {
   const float* beta_dev;         /* optional device fp32, replaces desc.beta             */
   const int32_t* cu_seqlens_m;   /* varlen-M plans: int32[L+1]                           */
   const int32_t* cu_seqlens_k;   /* varlen-K plans: int32[L+1]                           */
-  const int32_t* a_idx;          /* gather_a plans: int32[M]                             */
+  const int32_t* a_idx;          /* gather_a plans: int32[M] (varlen-M) or int32[K] (varlen-K) */
   int32_t* tile_counters;        /* NULL: static schedule; else as in gemm_run_dynamic  */
 } gemm_args;
 

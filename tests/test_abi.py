@@ -81,6 +81,9 @@ def test_create_accepts_valid(lib):
     # gathered A rows: A (gather_rows, K) K-major
     assert create(lib, base_desc(varlen_m=1, L=2, sb=65536, gather_a=1, gather_rows=1000)) == _abi.OK
     assert create(lib, base_desc(varlen_m=1, L=2, sb=65536, gather_a=1, gather_rows=10, b_major=_abi.COL)) == _abi.OK
+    # gathered k-rows of an M-major A (varlen-K)
+    d = base_desc(varlen_k=1, L=3, sd=65536, gather_a=1, gather_rows=1000, a_major=_abi.COL, b_major=_abi.COL)
+    assert create(lib, d) == _abi.OK
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -121,7 +124,9 @@ def test_create_accepts_valid(lib):
     (dict(varlen_k=1, varlen_m=1, L=2, sb=65536), _abi.INVALID_ARG),  # exclusive modes
     (dict(varlen_k=1, L=2, sd=65536, dact=1, c=2, ldc=256, sc=65536), _abi.UNSUPPORTED),
     (dict(gather_a=1, gather_rows=10), _abi.INVALID_ARG),  # gather without varlen
-    (dict(gather_a=1, gather_rows=10, varlen_k=1, L=2, sd=65536), _abi.UNSUPPORTED),  # gathered columns
+    (dict(gather_a=1, gather_rows=10, varlen_k=1, L=2, sd=65536), _abi.UNSUPPORTED),  # gathered columns of a K-major A
+    (dict(gather_a=1, gather_rows=300, varlen_k=1, L=2, sd=65536, a_major=_abi.COL, d_major=_abi.COL), _abi.UNSUPPORTED),
+    (dict(gather_a=1, gather_rows=1 << 22, varlen_k=1, L=2, sd=65536, a_major=_abi.COL), _abi.UNSUPPORTED),  # >= 2^31 B
     (dict(gather_a=2, varlen_m=1, L=2, sb=65536), _abi.INVALID_ARG),
     (dict(gather_a=1, gather_rows=-1, varlen_m=1, L=2, sb=65536), _abi.INVALID_ARG),
     (dict(gather_a=1, gather_rows=10, varlen_m=1, L=2, sb=65536, a_major=_abi.COL), _abi.UNSUPPORTED),

@@ -1,10 +1,11 @@
 """GPU parity of the grouped modes added to the persistent GEMM: variable-length K (grouped K,
-one output batch per group) and gathered A rows (varlen-M reading A through an index).
+one output batch per group) and gathered A (varlen-M reading A rows, varlen-K reading A columns
+through an index).
 
 Small cases span several tiles with ragged M / N and ragged or empty K groups, every major
 mode, both tiles, 16-bit and fp8 inputs, C with beta, activations and M-major outputs; they are
 compared element by element with the CPU oracle. Small integers must match exactly. The
-dynamic schedule must reproduce the static one bit for bit. The two grouped workloads run at
+dynamic schedule must reproduce the static one bit for bit. The grouped workloads run at
 full size with sampled outputs.
 """
 import ctypes
@@ -210,6 +211,74 @@ def test_gather_identity_equals_plain_varlen():
 
 
 # ---------------------------------------------------------------------------------------
+# gathered A columns (varlen-K)
+# ---------------------------------------------------------------------------------------
+
+def gather_k_small(sizes, M=264, N=392, cols_a=333, b_nmaj=True, seed=0, bad=False, c=False):
+    cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    K, G = int(cu[-1]), len(sizes)
+    r = np.random.Generator(np.random.PCG64(1400 + seed))
+    idx = r.integers(0, cols_a, size=max(K, 1)).astype(np.int32)[:K]
+    A = W.uniform(1401 + seed, (cols_a, M), "bf16").t()  # (M, cols_a), M-major
+    B = a2(N, K, b_nmaj, 1402 + seed, "bf16")
+    C = W.uniform(1403 + seed, (G, M, N), "f32") if c else None
+    if bad and K > 3:
+        idx[[0, K // 2, K - 1]] = [-1, cols_a, 1 << 30]
+    return W.Inputs("gather_k_small", M, N, K, G, "bf16", "bf16", A, B, C=C, c_dt="f32" if c else "none",
+                    d_dt="bf16", beta=0.5, cu_seqlens_k=cu, a_idx=idx)
+
+
+def oracle_view_k(inp):
+    """Out-of-range column indices mapped to an appended zero column of A."""
+    cols = inp.A.shape[1]
+    idx = inp.a_idx.copy()
+    out = (idx < 0) | (idx >= cols)
+    if not out.any():
+        return inp
+    A = torch.cat([inp.A.t(), torch.zeros((1, inp.M), dtype=inp.A.dtype)]).t()
+    idx[out] = cols
+    return W.Inputs(**{**inp.__dict__, "A": A, "a_idx": idx})
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+@pytest.mark.parametrize("b_nmaj", [True, False])
+@pytest.mark.parametrize("sizes", [[64, 0, 200, 8, 520], [0, 0, 136], [1024], [72, 64, 0]])
+def test_gather_k_small(tile, b_nmaj, sizes):
+    inp = gather_k_small(sizes, b_nmaj=b_nmaj, seed=len(sizes), c=len(sizes) == 3)
+    announce(f"gather-k tile={tile} b_nmaj={b_nmaj} sizes={sizes}")
+    d, _, _ = run_hip(inp, tile=tile)
+    pre, _ = problem_of(inp).all(*oracle_codes(inp))
+    check_close(d, pre, 2e-2, 1e-2, "D")
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_gather_k_any_split_and_bad_indices(tile):
+    # an N-major B takes group boundaries at any k; out-of-range indices read zero columns
+    inp = gather_k_small([5, 0, 131, 1, 77], bad=True, seed=9)
+    announce(f"gather-k bad indices tile={tile}")
+    d, _, _ = run_hip(inp, tile=tile)
+    ov = oracle_view_k(inp)
+    pre, _ = problem_of(ov).all(W.codes_of(ov.A), W.codes_of(ov.B), None)
+    check_close(d, pre, 2e-2, 1e-2, "D")
+
+
+def test_gather_k_identity_equals_plain_varlen_k():
+    inp = varlen_k_small([64, 0, 200, 8, 520], a_mmaj=True, b_nmaj=True, seed=11)
+    d_plain, _, _ = run_hip(inp)
+    inp.a_idx = np.arange(inp.K, dtype=np.int32)
+    d_g, _, _ = run_hip(inp)
+    assert np.array_equal(d_plain, d_g)
+
+
+def test_gather_k_dynamic_equals_static():
+    inp = gather_k_small([640, 8, 0, 1024, 72], M=1040, N=1296, cols_a=2000, seed=12)
+    d0, _, _ = run_hip(inp)
+    ctr = torch.zeros(8, dtype=torch.int32, device="cuda")
+    d1, _, _ = run_hip(inp, tile_counters=ctr)
+    assert np.array_equal(d0, d1)
+
+
+# ---------------------------------------------------------------------------------------
 # the grouped workloads at full size (sampled outputs, whole rows)
 # ---------------------------------------------------------------------------------------
 
@@ -219,3 +288,7 @@ def test_workload_varlen_k_moe():
 
 def test_workload_varlen_moe_gather():
     full_size(W.varlen_moe_gather(), npts=2000, rows=2)
+
+
+def test_workload_varlen_k_moe_gather():
+    full_size(W.varlen_k_moe_gather(), npts=2000, rows=1)

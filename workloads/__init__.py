@@ -256,6 +256,20 @@ def varlen_moe_gather(G=8, N=4096, K=4096, sizes=None, std=1.0 / 64.0, act="silu
     return inp
 
 
+def varlen_k_moe_gather(G=8, M=4096, N=4096, sizes=None, std=1.0, topk=2):
+    """The varlen-K workload with gathered A columns (the weight gradient read straight from
+    the unpermuted token matrix): X has sum(K_g) / topk token rows ~ N(0,1), stored
+    (tokens, M) row-major, so A = X^T is (M, tokens) M-major; a_idx names, for every routed
+    token of the expert-sorted problem, the token row it reads (seeded, uniform)."""
+    s = 1111 + 10 * 8
+    inp = varlen_k_moe(G, M, N, sizes, std)
+    tokens = max(1, inp.K // topk)
+    inp.A = normal(s + 0, (tokens, M), "bf16", std).t()
+    inp.a_idx = rng(s + 4).integers(0, tokens, size=inp.K).astype(np.int32)
+    inp.name = f"varlen_k_gather_{G}x{M}x{N}_bf16"
+    return inp
+
+
 WORKLOADS = {
     "plain_256": plain_256,
     "act_4096": act_4096,
@@ -267,6 +281,7 @@ WORKLOADS = {
     "dact_4096": dact_4096,
     "varlen_k_moe": varlen_k_moe,
     "varlen_moe_gather": varlen_moe_gather,
+    "varlen_k_moe_gather": varlen_k_moe_gather,
 }
 
 
