@@ -44,6 +44,7 @@ namespace gep {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -1048,6 +1049,60 @@ struct GemmKernel {
     }
   }
 
+  // ---- single 16-bit output without C: the values are final in the accumulator layout
+  // (alpha, then the activation for a PostAct output), so they are converted there and only
+  // the 16-bit results go through LDS: half the bytes of the fp32 path and the whole wave tile
+  // in one pass. Buffer: kWM rows of kWN 16-bit values, 16-byte chunk c of row r at c ^ swz(r),
+  // so that the 32 rows one accumulator write covers and the rows one read covers fall in
+  // distinct 16-byte slots of the 256-byte bank window.
+  static constexpr int kNC16 = kWN / 8;          // 16-byte chunks per row (8 or 16)
+  static constexpr int kRPI16 = 64 / kNC16;      // rows per read instruction
+  static constexpr bool kOnePass16 = kWM * kWN * 2 <= kEpiRegion;
+  static __device__ __forceinline__ int ebuf16(int r, int c) {
+    const int sw = kNC16 == 16 ? (r & 15) : ((r >> 1) & 7);
+    return r * (kWN * 2) + ((c ^ sw) << 4);
+  }
+
+  template <int DT, bool ACT>
+  static __device__ __forceinline__ void epilogue16(const KParams& p, const f32x16 (&acc)[kMI][kNI],
+                                                    GEP_LDS char* region, int lane, char* ob, int64_t ld,
+                                                    int rows_valid, int cols_valid, float alpha) {
+    // the LDS addresses below depend on the lane only; computed here (an opaque copy of the
+    // lane id), not hoisted to the kernel's start where they would stay live, and spill,
+    // across the main loop
+    asm volatile("" : "+v"(lane));
+    const int h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) {
+      const int lr = i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < kNI; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; g += 2) {
+          // groups g, g + 1: columns 32j + 8g + 4h + [0, 4) and the same 8 further
+          const f32x16& a = acc[i][j];
+          f32x8 v = f32x8{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3],
+                          a[4 * g + 4], a[4 * g + 5], a[4 * g + 6], a[4 * g + 7]} * alpha;
+          if constexpr (ACT) v = act8(p.act, v);
+          const i32x4 w = pack8<DT>(v);
+          *(GEP_LDS i32x2*)(region + ebuf16(lr, 4 * j + g) + 8 * h) = i32x2{w[0], w[1]};
+          *(GEP_LDS i32x2*)(region + ebuf16(lr, 4 * j + g + 1) + 8 * h) = i32x2{w[2], w[3]};
+          // one group pair at a time: keeps the converted values from crowding the registers
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    asm volatile("" ::: "memory");
+    const int rl = lane / kNC16, c = lane % kNC16;
+    const bool col_ok = 8 * c < cols_valid;
+#pragma unroll 4
+    for (int it = 0; it < kWM / kRPI16; ++it) {
+      const int r = it * kRPI16 + rl;
+      const i32x4 x = *(const GEP_LDS i32x4*)(region + ebuf16(r, c));
+      if (col_ok && r < rows_valid) *(i32x4*)(ob + ((int64_t)r * ld + 8 * c) * 2) = x;
+    }
+    asm volatile("" ::: "memory");
+  }
+
   static __device__ __forceinline__ void epilogue(const KParams& p, const TileInfo& ti,
                                                   const f32x16 (&acc)[kMI][kNI], GEP_LDS char* region, int lane,
                                                   int wm0, int wn0, float alpha, float beta) {
@@ -1062,6 +1117,25 @@ struct GemmKernel {
     ea.cols_valid = p.N - col0;
     ea.alpha = alpha;
     ea.beta = beta;
+    if constexpr (!DACT && kOnePass16) {
+      // no C and one 16-bit output: D = alpha acc, or PostAct = act(alpha acc)
+      if (p.c_dt == DT_NONE && (p.d_dt == DT_NONE) != (p.p_dt == DT_NONE)) {
+        const bool post = p.p_dt != DT_NONE;
+        const int ot = post ? p.p_dt : p.d_dt;
+        char* ob = post ? ea.pb : ea.db;
+        const int64_t ld = post ? p.ldp : p.ldd;
+        if (ot == DT_BF16) {
+          if (post && p.act != ACT_NONE) epilogue16<DT_BF16, true>(p, acc, region, lane, ob, ld, ea.rows_valid, ea.cols_valid, alpha);
+          else epilogue16<DT_BF16, false>(p, acc, region, lane, ob, ld, ea.rows_valid, ea.cols_valid, alpha);
+          return;
+        }
+        if (ot == DT_F16) {
+          if (post && p.act != ACT_NONE) epilogue16<DT_F16, true>(p, acc, region, lane, ob, ld, ea.rows_valid, ea.cols_valid, alpha);
+          else epilogue16<DT_F16, false>(p, acc, region, lane, ob, ld, ea.rows_valid, ea.cols_valid, alpha);
+          return;
+        }
+      }
+    }
     // one output type for C, D and PostAct (those present), 16-bit: the branch-free path
     const int ot = p.d_dt != DT_NONE ? p.d_dt : p.p_dt;
     const bool same = (p.c_dt == DT_NONE || p.c_dt == ot) && (p.p_dt == DT_NONE || p.p_dt == ot);
