@@ -514,12 +514,17 @@ struct GemmKernel {
   // MFMA steps, kCPF chunks next to each fragment read
   static constexpr int kChunksPerKt = LA::kInstr + LB::kInstr;
   static constexpr int kWriteSteps = kDMA ? 1 : (kSteps >= 4 ? 2 : 1);
-  static constexpr int kChunksPerStep = kChunksPerKt / kWriteSteps;
+  // 16-bit global -> LDS transfers of a k-tile are issued in two halves: the first after the
+  // barrier that frees its stage, the second in the first step of the next k-tile (see ktile).
+  // fp8 keeps one: its last step holds twice the MFMA work and covers the transfers (split,
+  // fp8 8192^3 measured 8% slower).
+  static constexpr int kDmaParts = (kDMA && kES == 2) ? 2 : 1;
+  static constexpr int kChunksPerStep = kChunksPerKt / kWriteSteps / kDmaParts;
   // fragment slot f carries MFMAs [mlo(f), mlo(f+1)) and register chunks [clo(f), clo(f+1))
   static constexpr int mlo(int f) { return f * kMfmaPerStep / kFrags; }
   static constexpr int clo(int f) { return f * kChunksPerStep / kFrags; }
   static_assert(kSteps % 2 == 0, "a k-tile ends on fragment buffer 0");
-  static_assert(kChunksPerKt % kWriteSteps == 0, "register chunks must spread evenly over the write steps");
+  static_assert(kChunksPerKt % (kWriteSteps * kDmaParts) == 0, "register chunks must spread evenly over the write steps");
   static_assert(kMfmaPerStep >= kFrags, "every fragment slot needs an MFMA");
 
   // ---- scheduling hints: one slot per fragment, each carrying its MFMAs, the fragment's
@@ -824,15 +829,25 @@ struct GemmKernel {
     GEP_LDS char* nxt = smem + (PAR ^ 1) * kStageBytes;
     const KtSrc src = kt_src(p, ti, kt + 2);
     if constexpr (kDMA) {
-      // stage PAR^1 (k-tile kt+1) was filled by transfers issued in the last step of k-tile
-      // kt-1; k-tile kt+2 goes into stage PAR once its last fragments have been read
+      // Stage PAR^1 (k-tile kt+1) received the first half of its transfers in the last step of
+      // k-tile kt-1 and (16-bit) gets the second half in step 0 here (nobody reads it before
+      // this k-tile's barrier, which waits for both); k-tile kt+2 goes into stage PAR once its
+      // last fragments have been read, its first half in the last step. Issued in one step, the
+      // 64 KB of a k-tile held the transfer step at ~930-1000 cycles against 512 of MFMA work
+      // (bf16; the address path takes ~15 cycles per 1 KB instruction per CU). Same-box runs:
+      // 4096^3 with C / D / GELU PostAct +1.9%, other workloads within +-0.4% (the power-limited
+      // clock takes back the cycles saved).
+      if constexpr (kDmaParts == 2)
+        step<0, true, kChunksPerStep>(acc, fa, fb, cur, 1, la, lb, nxt, kt_src(p, ti, kt + 1), wave, lane, wm0, wn0);
+      else
+        step<0, false, 0>(acc, fa, fb, cur, 1, la, lb, nxt, src, wave, lane, wm0, wn0);
       // The steps before kPrioSplit run at wave priority 1 (set after the previous barrier),
       // the rest at 0: on a SIMD shared by two waves the issue arbiter favours the older wave,
       // which otherwise runs ahead and leaves its partner to finish each k-tile alone;
       // yielding once ahead keeps the pair level (measured: the older waves' barrier time per
       // 256x256 tile of the 8192^3 GEMM 120 K -> 47 K cycles, +0.3-1.9% on every 8-wave
       // workload; with one wave per SIMD it changes nothing).
-      first_steps_range<0, kPrioSplit>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+      first_steps_range<1, kPrioSplit>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
@@ -1328,7 +1343,7 @@ struct GemmKernel {
         if constexpr (kDMA) {
           // k-tiles 0 and 1 -> stages 0 and 1
           dma_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 0), wave);
-          dma_chunks<0, kChunksPerKt>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);
+          dma_chunks<0, kChunksPerStep>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);  // (half)
           dma_barrier();
         } else {
           // k-tile 0 -> stage 0, registers <- k-tile 1
