@@ -1284,6 +1284,15 @@ struct GemmKernel {
         U = split ? 4 * rem : 0;
       }
     }
+    // The quarter-tile launch can hold more workgroups than items (a varlen grid is sized
+    // before T is known): its XCD queues then take ceil(U / 8) consecutive items each, so the
+    // items spread over all eight XCDs rather than filling the first queues (the workgroups
+    // past them take none).
+    int b0 = bb;
+    if (p.tail == 2 && xq && U <= P) {
+      const int Qu = (U + 7) >> 3;
+      b0 = qj < Qu ? qx * Qu + qj : U;
+    }
 
     const float alpha = p.alpha_ptr ? *p.alpha_ptr : p.alpha;
     const float beta = p.beta_ptr ? *p.beta_ptr : p.beta;
@@ -1313,9 +1322,9 @@ struct GemmKernel {
     const int q_tiles = (U / P) * Q + min(max(U % P - qx * Q, 0), Q);
     int32_t fetched = 0;
 
-    if (bb < U) begin_tile(bb);
+    if (b0 < U) begin_tile(b0);
     int iter = 0;
-    for (int t = bb; t < U; ++iter) {
+    for (int t = b0; t < U; ++iter) {
       // claim the tile after this one (its result is first waited for where it is published)
       if (ctr && tid == 0) fetched = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (ti.m0 >= ti.row_end || ti.n0 >= p.N) {  // a quarter tile wholly outside the output
