@@ -8,6 +8,13 @@ The same line also reports the fp8 (e4m3 x e5m2) 8192^3 and varlen-M grouped wor
 the roofline of the dominant kernel and the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
+                    [--cold N]
+
+`roofline.attainable_us` is the time at the roofline, max(FLOPs / MFMA peak, algorithmic
+bytes / 8 TB/s), summed per group for grouped workloads (small groups can be HBM-bound on
+their B read); `frac_of_attainable` compares the measured time with it. `--cold N` times the
+primary workload rotating N input sets (the pages' cold-L2 option; N = 4 holds over 1 GB for
+8192^3 bf16, more than the 256 MB MALL); the default is warm.
 """
 import argparse
 import hashlib
@@ -55,6 +62,30 @@ def algorithmic_bytes(inp):
     return a + b + mn * (es[inp.c_dt] + es[inp.d_dt] + es[inp.post_dt])
 
 
+def attainable_s(inp):
+    """Seconds at the roofline: max(FLOPs / MFMA peak, algorithmic bytes / HBM peak), summed
+    over the groups of a grouped problem (a small group can be HBM-bound on its B read while
+    the whole problem is not)."""
+    es = {"f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e5m2": 1, "none": 0}
+    peak = PEAK_TFLOPS[inp.a_dt] * 1e12
+    hbm = HBM_PEAK_GBS * 1e9
+    out_b = es[inp.c_dt] + es[inp.d_dt] + es[inp.post_dt]
+
+    def roof(fl, by):
+        return max(fl / peak, by / hbm)
+    if inp.varlen:
+        ms = [int(x) for x in (inp.cu_seqlens[1:] - inp.cu_seqlens[:-1])]
+        return sum(roof(2.0 * m * inp.N * inp.K,
+                        m * inp.K * es[inp.a_dt] + inp.N * inp.K * es[inp.b_dt] + m * inp.N * out_b)
+                   for m in ms)
+    if inp.cu_seqlens_k is not None:
+        ks = [int(x) for x in (inp.cu_seqlens_k[1:] - inp.cu_seqlens_k[:-1])]
+        return sum(roof(2.0 * inp.M * inp.N * k,
+                        (inp.M * es[inp.a_dt] + inp.N * es[inp.b_dt]) * k + inp.M * inp.N * out_b)
+                   for k in ks)
+    return roof(inp.flops(), algorithmic_bytes(inp))
+
+
 def setup(name, **tuning):
     import torch
     import workloads as W
@@ -74,6 +105,27 @@ def setup(name, **tuning):
     if cuk is not None or idx is not None:
         plan = _Bound(plan, cu_seqlens_k=cuk, a_idx=idx)
     return inp, plan, args
+
+
+class _Rotating:
+    """Runs the plan on input set i % n at call i (--cold: more input bytes than the 256 MB
+    MALL, so that every launch reads its operands from HBM)."""
+
+    def __init__(self, plan, sets):
+        self.plan, self.sets, self.i = plan, sets, 0
+
+    def run(self, *_):
+        self.plan.run(*self.sets[self.i % len(self.sets)])
+        self.i += 1
+
+
+def cold_sets(args, n):
+    """n input sets: the given one and n - 1 copies of its A, B and C (outputs shared)."""
+    sets = [args]
+    for _ in range(n - 1):
+        A, B, C = (None if x is None else x.clone() for x in args[:3])
+        sets.append((A, B, C) + tuple(args[3:]))
+    return sets
 
 
 class _Bound:
@@ -205,6 +257,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA rate probe")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cold", type=int, default=0, metavar="N",
+                    help="rotate N copies of the primary workload's inputs (cold MALL / L2); 0: warm")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for traffic counters)")
     a = ap.parse_args()
@@ -230,7 +284,12 @@ def main():
     tm, tn, G, xcd, T, P = plan.grid()
     torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ms = time_plan(plan, args, a.steps, a.warmup, SETTLE_S)
+    if a.cold > 1:
+        timed = _Rotating(plan, cold_sets(args, a.cold))
+        ms = time_plan(timed, args, a.steps, a.warmup, SETTLE_S)
+        del timed
+    else:
+        ms = time_plan(plan, args, a.steps, a.warmup, SETTLE_S)
     flops = inp.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[inp.a_dt]
@@ -238,7 +297,9 @@ def main():
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(tflops / peak, 4), "traffic": traffic,
             "kernel": "gemm_persistent_kernel", "algorithmic_bytes": algorithmic_bytes(inp),
-            "hbm_gbs_algorithmic": round(algorithmic_bytes(inp) / (ms * 1e-3) / 1e9, 1)}
+            "hbm_gbs_algorithmic": round(algorithmic_bytes(inp) / (ms * 1e-3) / 1e9, 1),
+            "attainable_us": round(attainable_s(inp) * 1e6, 1),
+            "frac_of_attainable": round(attainable_s(inp) / (ms * 1e-3), 4)}
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -246,7 +307,8 @@ def main():
            "config": {"workload": inp.name, "M": inp.M, "N": inp.N, "K": inp.K, "L": inp.L,
                       "tile": [tm, tn], "group_m": G, "xcd_remap": xcd,
                       "raster": "n" if plan.raster_along_n() else "m", "tiles": T, "grid": P,
-                      "settle_s": SETTLE_S, "pct_of_peak": round(100 * tflops / peak, 2)},
+                      "settle_s": SETTLE_S, "cold_sets": max(a.cold, 0) if a.cold > 1 else 0,
+                      "pct_of_peak": round(100 * tflops / peak, 2)},
            "roofline": roof}
     del args, plan
     if not a.no_ceiling:
@@ -265,7 +327,8 @@ def main():
             t2 = i2.flops() / (ms2 * 1e-3) / 1e12
             sec[name] = {"tflops": round(t2, 2), "ms": round(ms2, 4),
                          "pct_of_peak": round(100 * t2 / PEAK_TFLOPS[i2.a_dt], 2),
-                         "peak": PEAK_TFLOPS[i2.a_dt], "dtype": i2.a_dt}
+                         "peak": PEAK_TFLOPS[i2.a_dt], "dtype": i2.a_dt,
+                         "frac_of_attainable": round(attainable_s(i2) / (ms2 * 1e-3), 4)}
             del p2, a2, i2
             torch.cuda.empty_cache()
         out["secondary"] = sec
