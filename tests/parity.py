@@ -56,7 +56,7 @@ def run_hip(inp, d_major_m=False, tile=None, alpha_dev=None, beta_dev=None, tile
 
 
 def check_close(got, want, tol, rms_tol, what=""):
-    """Spec bound per element plus the normalised-RMS guard."""
+    """Per element |got - want| <= tol (|want| + 1), plus the normalised-RMS guard."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
