@@ -273,7 +273,7 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the GEMM shards without communication; see the design notes). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

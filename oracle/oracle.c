@@ -27,7 +27,8 @@
 /* Element types (oracle-local numbering; the Python wrapper maps names to these). */
 enum { ORC_NONE = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_F32 = 3, ORC_E4M3 = 4, ORC_E5M2 = 5 };
 /* Activations: page 6, quack/gemm_act_sm90.py, act_fn_map (none, relu, relu_sq,
- * gelu_tanh_approx); SiLU is added by this build's workload list. */
+ * gelu_tanh_approx). SiLU, x * sigmoid(x) by its standard definition, is not in that map:
+ * the grouped MoE workload's epilogue uses it. */
 enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_RELU_SQ = 2, ORC_ACT_GELU_TANH = 3, ORC_ACT_SILU = 4 };
 
 /* ------------------------------------------------------------------------------------ */
