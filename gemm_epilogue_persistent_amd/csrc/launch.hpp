@@ -15,7 +15,10 @@ constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
 // waves (two per SIMD, 128x64 accumulators each) with global -> LDS transfers: measured +2%
 // on the 8192^3 GEMM, +4% on the 4096^3 GEMM with C and GELU, +0.5-2.5% on varlen-M (its
 // epilogue halves; the store drain moves into the next tile's first wait). Every other kernel
-// runs 4: transfers slowed the M/N-major one by ~30%.
+// runs 4. With 8 waves and transfers the M/N-major kernels ran at half speed (batched
+// 2048x2048x4096x16 550 vs 1125 TFLOP/s, varlen-K 544 vs 1108): their transposed fragment
+// reads (two ds_read_b64_tr_b16 per fragment) grow to 1.5x as many per CU with 128x64 wave
+// tiles and bound the loop.
 template <int BM, int OP, bool AK, bool BK>
 constexpr int waves() { return (BM == 256 && OP != OP_FP8 && AK && BK) ? 8 : 4; }
 
