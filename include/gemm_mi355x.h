@@ -146,7 +146,7 @@ typedef enum {
  *                   skipped). Varlen plans decide on the device, where T is known; their
  *                   second launch exits at once when there is no such tail. Same results.
  *                   gemm_run_logged never splits.
- *   raster_order    0: default (along N for dense L == 1, else along M), 1: along M,
+ *   raster_order    0: default (along N for dense L == 1 with C, else along M), 1: along M,
  *                   2: along N (dense only). The grouped
  *                   raster takes groups of group_m blocks along M, M fastest inside a group
  *                   (page 5's swizzle); along N the roles of M and N are exchanged (page 6,

@@ -173,6 +173,27 @@ def test_plan_grid(lib):
     assert grid_of(lib, base_desc(M=2048, N=2048, K=64, lda=64, ldb=64, ldd=2048))[5] == 256
 
 
+def raster_of(lib, d):
+    h = ctypes.c_void_p()
+    assert lib.gemm_create(ctypes.byref(d), ctypes.byref(h)) == _abi.OK
+    v = ctypes.c_int32(-1)
+    assert lib.gemm_plan_raster(h, ctypes.byref(v)) == _abi.OK
+    lib.gemm_destroy(h)
+    return v.value
+
+
+def test_default_raster_order():
+    """Along N only for a single dense GEMM that reads C; an explicit order always wins."""
+    lib = _abi.load()
+    big = dict(M=8192, N=8192, K=8192, lda=8192, ldb=8192, ldd=8192)
+    assert raster_of(lib, base_desc(**big)) == 0
+    assert raster_of(lib, base_desc(**big, c=_abi.DT["bf16"], ldc=8192)) == 1
+    assert raster_of(lib, base_desc(**big, c=_abi.DT["bf16"], ldc=8192, raster_order=1)) == 0
+    assert raster_of(lib, base_desc(**big, raster_order=2)) == 1
+    assert raster_of(lib, base_desc(**big, c=_abi.DT["bf16"], ldc=8192, L=2, sa=8192 * 8192,
+                                    sb=8192 * 8192, sc=8192 * 8192, sd=8192 * 8192)) == 0
+
+
 def test_fastdivmod_constants_match_oracle(lib):
     m = ctypes.c_uint32()
     s = ctypes.c_uint32()
