@@ -247,6 +247,11 @@ def traffic_for(name):
     return int(rec["hbm_bytes_per_launch"])
 
 
+def progress(msg):
+    """A progress line on stderr (stdout carries only the JSON result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +297,7 @@ def main():
         ms = time_plan(plan, args, a.steps, a.warmup, SETTLE_S)
     flops = inp.flops()
     tflops = flops / (ms * 1e-3) / 1e12
+    progress(f"{a.workload}: {ms * 1e3:.1f} us per step, {tflops:.1f} TFLOP/s")
     peak = PEAK_TFLOPS[inp.a_dt]
     traffic = traffic_for(a.workload)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
@@ -314,6 +320,7 @@ def main():
     if not a.no_ceiling:
         # the practical MFMA ceiling on full-entropy data at the clock the part sustains
         ceil = {d: mfma_ceiling(d, PEAK_TFLOPS[d]) for d in ("bf16", "e4m3")}
+        progress(f"MFMA ceiling probe: {ceil['bf16']['tflops']} (bf16), {ceil['e4m3']['tflops']} (fp8) TFLOP/s")
         out["mfma_ceiling"] = ceil
         c = ceil["e4m3" if inp.a_dt in ("e4m3", "e5m2") else "bf16"]
         roof["frac_of_mfma_ceiling"] = round(tflops / c["tflops"], 4)
@@ -325,6 +332,7 @@ def main():
             i2, p2, a2 = setup(name)
             ms2 = time_plan(p2, a2, max(10, a.steps // 3), max(2, a.warmup // 2), SETTLE_S)
             t2 = i2.flops() / (ms2 * 1e-3) / 1e12
+            progress(f"{name}: {ms2 * 1e3:.1f} us per step, {t2:.1f} TFLOP/s")
             sec[name] = {"tflops": round(t2, 2), "ms": round(ms2, 4),
                          "pct_of_peak": round(100 * t2 / PEAK_TFLOPS[i2.a_dt], 2),
                          "peak": PEAK_TFLOPS[i2.a_dt], "dtype": i2.a_dt,
@@ -333,6 +341,7 @@ def main():
             torch.cuda.empty_cache()
         out["secondary"] = sec
     if not a.no_cpu_baseline:
+        progress(f"CPU oracle on a sample of {a.workload} (~{a.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(inp, a.cpu_budget)
     print(json.dumps(out), flush=True)
 
