@@ -1071,6 +1071,8 @@ struct GemmKernel {
   // so that the 32 rows one accumulator write covers and the rows one read covers fall in
   // distinct 16-byte slots of the 256-byte bank window.
   static constexpr int kNC16 = kWN / 8;          // 16-byte chunks per row (8 or 16)
+  // (the swizzle key below spans 8 or 16 chunks: a narrower row would need it masked)
+  static_assert(kNC16 == 8 || kNC16 == 16, "single-output epilogue rows hold 8 or 16 chunks");
   static constexpr int kRPI16 = 64 / kNC16;      // rows per read instruction
   static constexpr bool kOnePass16 = kWM * kWN * 2 <= kEpiRegion;
   static __device__ __forceinline__ int ebuf16(int r, int c) {
