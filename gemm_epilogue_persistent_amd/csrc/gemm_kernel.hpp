@@ -1045,19 +1045,22 @@ struct GemmKernel {
     }
   }
 
+  // Each lane covers 8 columns as two 4-column halves, each checked on its own: with only
+  // f32 outputs the contiguous extent is a multiple of 4 elements, so the right edge may
+  // end after the first half.
   static __device__ __forceinline__ void pass_generic(const KParams& p, const EpiArgs& ea, const GEP_LDS char* buf,
                                                       int m0, int lane) {
     const int rl = lane / kNC8, c8 = lane % kNC8;
     const int esc = dt_bytes(p.c_dt), esd = dt_bytes(p.d_dt), esp = dt_bytes(p.p_dt);
-    const bool col_ok = 8 * c8 < ea.cols_valid;
 #pragma unroll 1
     for (int it = 0; it < kIt; ++it) {
       const int r = it * kRPI + rl, m = m0 + r;
-      if (!(col_ok && m < ea.rows_valid)) continue;
+      if (m >= ea.rows_valid) continue;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const f32x4 x = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, hf));
         const int n = 8 * c8 + 4 * hf;
+        if (n + 4 > ea.cols_valid) continue;
+        const f32x4 x = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, hf));
         finish4(p, ea.cb + ((int64_t)m * p.ldc + n) * esc, ea.db + ((int64_t)m * p.ldd + n) * esd,
                 ea.pb + ((int64_t)m * p.ldp + n) * esp, x, ea.alpha, ea.beta);
       }

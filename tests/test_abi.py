@@ -207,3 +207,18 @@ def test_status_strings(lib):
     for st in range(6):
         assert lib.gemm_status_string(st)
     assert lib.gemm_status_string(99) == b"unknown status"
+
+
+def test_f32_output_granularity(lib):
+    """f32-only outputs need their contiguous extent in whole 16-byte chunks, i.e. a multiple
+    of 4 elements (not 8): N = 260 is accepted for N-major f32 outputs and M = 260 for
+    M-major ones; the kernel then stores the last 4-column half of the right-edge tile only
+    where it exists. 16-bit outputs at the same extent, and f32 at 258, are rejected."""
+    f32 = _abi.DT["f32"]
+    assert create(lib, base_desc(N=260, d=f32, ldd=260)) == _abi.OK
+    assert create(lib, base_desc(N=260, c=f32, ldc=272, d=f32, ldd=264, post=f32, ldp=260,
+                                 act=_abi.ACT["relu"])) == _abi.OK
+    assert create(lib, base_desc(M=260, d=f32, ldd=260, d_major=_abi.COL)) == _abi.OK
+    assert create(lib, base_desc(N=260, ldd=264)) == _abi.ALIGNMENT  # bf16 D: 520 bytes
+    assert create(lib, base_desc(N=260, d=f32, ldd=264, post=_abi.DT["bf16"], ldp=264)) == _abi.ALIGNMENT
+    assert create(lib, base_desc(N=258, d=f32, ldd=260)) == _abi.ALIGNMENT

@@ -1,0 +1,98 @@
+"""GPU parity at the edges of what gemm_create accepts, with guard bands around the outputs.
+
+f32-only outputs need their contiguous extent in whole 16-byte chunks, i.e. a multiple of 4
+elements: at N = 260 (N-major) or M = 260 (M-major) the right-edge tile ends half way
+through a lane's 8-column group. Every output here lives inside a larger buffer prefilled
+with a sentinel: 12 padding elements past each contiguous row (ld = extent + 12) and one
+trailing row per batch. After the run the padding must still hold the sentinel and every
+output element must match the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity import check_close, oracle_codes, problem_of, to_dev, tol_for
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 12345.0
+
+
+def announce(name):
+    print(f"[case] {name}", flush=True)
+    sys.stdout.flush()
+
+
+def guarded(L, M, N, dt, m_major):
+    """A logical (L, M, N) view into a sentinel-filled buffer with padded rows and a trailing
+    guard row; returns (view, buffer, mask of the view's elements inside the buffer)."""
+    rows, cols = (N, M) if m_major else (M, N)
+    buf = torch.full((L, rows + 1, cols + 12), SENTINEL, dtype=W.TORCH_DT[dt], device="cuda")
+    v = buf[:, :rows, :cols]
+    view = v.permute(0, 2, 1) if m_major else v
+    mask = np.zeros((L, rows + 1, cols + 12), dtype=bool)
+    mask[:, :rows, :cols] = True
+    return view, buf, mask
+
+
+def run_guarded(inp, m_major, tile, dact=False):
+    from gemm_epilogue_persistent_amd import Plan
+    A, B, C = to_dev(inp.A), to_dev(inp.B), to_dev(inp.C)
+    D, dbuf, mask = guarded(inp.L, inp.M, inp.N, inp.d_dt, m_major)
+    P = pbuf = None
+    if inp.post_dt != "none":
+        P, pbuf, _ = guarded(inp.L, inp.M, inp.N, inp.post_dt, m_major)
+    plan = Plan(A, B, C, D, P, inp.alpha, inp.beta, inp.act, tile=tile, dact=dact)
+    plan.run(A, B, C, D, P)
+    torch.cuda.synchronize()
+    for buf in (dbuf, pbuf):
+        if buf is not None:
+            pad = buf.cpu().double().numpy()[~mask]
+            assert (pad == SENTINEL).all(), f"{(pad != SENTINEL).sum()} guard elements overwritten"
+    d = D.double().cpu().numpy()
+    p = None if P is None else P.double().cpu().numpy()
+    return d, p
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+@pytest.mark.parametrize("m_major", [False, True])
+@pytest.mark.parametrize("act", ["none", "gelu_tanh"])
+def test_f32_outputs_ragged_half_group(tile, m_major, act):
+    # the output's contiguous extent is 260 = 8 * 32 + 4 elements
+    M, N = (260, 392) if m_major else (392, 260)
+    L, K = 2, 136
+    A = W.make_a(W.uniform, L, M, K, False, 2100, "bf16")
+    B = W.make_b(W.uniform, L, N, K, m_major, 2101, "bf16")  # N-major only where N = 392
+    # C with padded rows too (its own leading dimension)
+    rows, cols = (N, M) if m_major else (M, N)
+    cstore = W.uniform(2102, (L, rows, cols + 8), "f32")[:, :, :cols]
+    C = cstore.permute(0, 2, 1) if m_major else cstore
+    post = "f32" if act != "none" else "none"
+    inp = W.Inputs("f32_edge", M, N, K, L, "bf16", "bf16", A, B, C=C, c_dt="f32", d_dt="f32",
+                   post_dt=post, alpha=0.75, beta=-0.5, act=act)
+    announce(f"f32 outputs M={M} N={N} tile={tile} m_major={m_major} act={act}")
+    d, p = run_guarded(inp, m_major, tile)
+    pre, postv = problem_of(inp).all(*oracle_codes(inp))
+    tol, rms = tol_for(inp)
+    check_close(d, pre, tol, rms, "D")
+    if p is not None:
+        check_close(p, postv, tol, rms, "PostAct")
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_f32_dact_ragged_half_group(tile):
+    M, N, K, L = 200, 260, 72, 1
+    A = W.normal(2110, (L, M, K), "bf16", 0.5)
+    B = W.normal(2111, (L, N, K), "bf16", 0.5)
+    C = W.normal(2112, (L, M, N), "f32", 1.5)
+    inp = W.Inputs("f32_dact_edge", M, N, K, L, "bf16", "bf16", A, B, C=C, c_dt="f32", d_dt="f32",
+                   post_dt="f32", act="silu", dact=True)
+    announce(f"f32 dact N={N} tile={tile}")
+    d, p = run_guarded(inp, False, tile, dact=True)
+    pre, postv = problem_of(inp).all(*oracle_codes(inp))
+    tol, rms = tol_for(inp)
+    check_close(d, pre, tol, rms, "D")
+    check_close(p, postv, tol, rms, "PostAct")

@@ -32,15 +32,13 @@ def draw_case(i):
     a_dt = b_dt = dt
     if fp8:
         a_dt, b_dt = [("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e4m3", "e4m3"), ("e5m2", "e5m2")][int(r.integers(0, 4))]
-    unit = 16  # contiguous extents: whole 16-byte chunks for every element size used here
     a_mmaj = not fp8 and bool(r.random() < 0.5)
     b_nmaj = not fp8 and bool(r.random() < 0.5)
     if mode == "varlen_m":
         a_mmaj = False  # its A rows are ragged: M-contiguous storage would not be whole chunks
     if gather and mode == "varlen_k":
         a_mmaj = True
-    M, N = aligned(r, 16, 560, unit), aligned(r, 16, 560, unit)
-    out_dt = ["bf16", "f16", "f32"][int(r.integers(0, 3))]
+    out_dt = ["bf16", "f16", "f32", "f32"][int(r.integers(0, 4))]
     c_dt = "none" if r.random() < 0.5 else ["bf16", "f16", "f32"][int(r.integers(0, 3))]
     if c_dt != "none" and c_dt != "f32" and out_dt != "f32":
         c_dt = out_dt
@@ -54,6 +52,18 @@ def draw_case(i):
     seed = 9100 + 10 * i
     es = 1 if fp8 else 2
     kunit = 16 // es
+    # M and N at the granularity gemm_create accepts: a contiguous extent holds whole
+    # 16-byte chunks (4 f32, 8 16-bit elements); extents that are not contiguous anywhere
+    # are free
+    out_unit = max(16 // W.ELEM_BYTES[t] for t in (out_dt, c_dt) if t != "none")
+    n_unit = (out_unit if not m_major_out else 1)
+    if b_nmaj:
+        n_unit = max(n_unit, 16 // es)
+    m_unit = out_unit if m_major_out else 1
+    if a_mmaj:
+        m_unit = max(m_unit, 16 // es)
+    M, N = aligned(r, 16, 560, m_unit), aligned(r, 16, 560, n_unit)
+    k_free = mode == "dense" and a_mmaj and b_nmaj  # K contiguous in neither operand
 
     scales = []  # fp8: per-tensor scales, folded into alpha so outputs stay O(sqrt(K))
 
@@ -69,7 +79,7 @@ def draw_case(i):
 
     if mode == "dense":
         L = int(r.integers(1, 4))
-        K = aligned(r, 0, 520, kunit) if r.random() < 0.9 else 0
+        K = aligned(r, 0, 520, 1 if k_free else kunit) if r.random() < 0.9 else 0
         if fp8:
             K = max(K, kunit)  # per-tensor fp8 scales need a non-empty operand
         if fp8:

@@ -25,6 +25,7 @@ TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32,
 CODE_DT = {"f16": torch.int16, "bf16": torch.int16, "f32": torch.int32,
            "e4m3": torch.uint8, "e5m2": torch.uint8}
 FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "f32": 4, "e4m3": 1, "e5m2": 1}
 
 
 @dataclass
@@ -300,15 +301,15 @@ def to_dev(t):
     return torch.as_strided(dbase, t.size(), t.stride(), t.storage_offset())
 
 
-def out_like(inp, dt, m_major=False, fill=float("nan")):
+def out_like(inp, dt, m_major=False, fill=float("nan"), device="cuda"):
     """Output (L, M, N) (varlen: (M, N)) of type dt on the GPU, N- or M-contiguous,
     pre-filled with `fill` so that unwritten elements show."""
     tdt = TORCH_DT[dt]
     if inp.varlen:
-        t = torch.empty((inp.N, inp.M), dtype=tdt, device="cuda").t() if m_major else \
-            torch.empty((inp.M, inp.N), dtype=tdt, device="cuda")
+        t = torch.empty((inp.N, inp.M), dtype=tdt, device=device).t() if m_major else \
+            torch.empty((inp.M, inp.N), dtype=tdt, device=device)
     else:
-        t = torch.empty((inp.L, inp.N, inp.M), dtype=tdt, device="cuda").permute(0, 2, 1) if m_major \
-            else torch.empty((inp.L, inp.M, inp.N), dtype=tdt, device="cuda")
+        t = torch.empty((inp.L, inp.N, inp.M), dtype=tdt, device=device).permute(0, 2, 1) if m_major \
+            else torch.empty((inp.L, inp.M, inp.N), dtype=tdt, device=device)
     t.fill_(fill)
     return t
