@@ -36,7 +36,18 @@ class _Problem(ctypes.Structure):
         ("varlen_k", ctypes.c_int32),
         ("cu_seqlens_k", ctypes.POINTER(ctypes.c_int32)),
         ("a_idx", ctypes.POINTER(ctypes.c_int32)),
+        ("a_rows", ctypes.c_int64),
     ]
+
+
+_ERRORS = {-1: "cu_seqlens must start at 0, never decrease and end at M",
+           -2: "cu_seqlens_k must start at 0, never decrease and end at most at K",
+           -3: "requested output coordinates lie outside the output"}
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError(f"oracle: {_ERRORS.get(rc, rc)}")
 
 
 _lib = None
@@ -144,10 +155,15 @@ class Problem:
 
     def __init__(self, M, N, K, L, a_dt, b_dt, a_kmajor=True, b_kmajor=True, lda=None, ldb=None,
                  sa=0, sb=0, c_dt="none", c_nmajor=True, ldc=None, sc=0, alpha=1.0, beta=1.0,
-                 act="none", cu_seqlens=None, dact=False, cu_seqlens_k=None, a_idx=None):
+                 act="none", cu_seqlens=None, dact=False, cu_seqlens_k=None, a_idx=None,
+                 a_rows=None):
         """Varlen-K: cu_seqlens_k (L+1 entries) splits K into groups, A (M, K) and B (N, K)
         have no batch index, K is A's and B's total K extent. a_idx (varlen-M or varlen-K
-        only): the A row of each global output row, or the A column of each global k."""
+        only): the A row of each global output row, or the A column of each global k;
+        a_rows: the number of rows (varlen-M) or columns (varlen-K) of A an index may name
+        (an index outside [0, a_rows) reads zeros). Invalid cu_seqlens / cu_seqlens_k raise
+        ValueError when the problem is evaluated."""
+        assert a_idx is None or a_rows is not None, "a gathered A needs its row (column) count"
         assert cu_seqlens is None or cu_seqlens_k is None, "varlen in M or in K, not both"
         assert a_idx is None or cu_seqlens is not None or cu_seqlens_k is not None, \
             "gathered A needs varlen-M or varlen-K"
@@ -164,6 +180,7 @@ class Problem:
         self.cu_seqlens = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
         self.cu_seqlens_k = None if cu_seqlens_k is None else np.ascontiguousarray(cu_seqlens_k, dtype=np.int32)
         self.a_idx = None if a_idx is None else np.ascontiguousarray(a_idx, dtype=np.int32)
+        self.a_rows = 0 if a_rows is None else int(a_rows)
 
     def _struct(self):
         s = _Problem()
@@ -186,6 +203,7 @@ class Problem:
             s.cu_seqlens_k = self.cu_seqlens_k.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         if self.a_idx is not None:
             s.a_idx = self.a_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        s.a_rows = self.a_rows
         return s
 
     @staticmethod
@@ -200,9 +218,9 @@ class Problem:
         pts = np.ascontiguousarray(pts, dtype=np.int64).reshape(-1, 3)
         pre = np.empty(len(pts)); post = np.empty(len(pts))
         s = self._struct()
-        _load().orc_gemm_points(ctypes.byref(s), self._ptr(A), self._ptr(B), self._ptr(C),
+        _check(_load().orc_gemm_points(ctypes.byref(s), self._ptr(A), self._ptr(B), self._ptr(C),
                                 len(pts), pts.ctypes.data, pre.ctypes.data, post.ctypes.data,
-                                nthreads)
+                                nthreads))
         return pre, post
 
     def rows(self, A, B, C, rows, nthreads=0):
@@ -210,9 +228,9 @@ class Problem:
         rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
         pre = np.empty((len(rows), self.N)); post = np.empty((len(rows), self.N))
         s = self._struct()
-        _load().orc_gemm_rows(ctypes.byref(s), self._ptr(A), self._ptr(B), self._ptr(C),
+        _check(_load().orc_gemm_rows(ctypes.byref(s), self._ptr(A), self._ptr(B), self._ptr(C),
                               len(rows), rows.ctypes.data, pre.ctypes.data, post.ctypes.data,
-                              nthreads)
+                              nthreads))
         return pre, post
 
     def all(self, A, B, C, nthreads=0):
@@ -220,8 +238,8 @@ class Problem:
         shape = (self.M, self.N) if self.cu_seqlens is not None else (self.L, self.M, self.N)
         pre = np.empty(shape); post = np.empty(shape)
         s = self._struct()
-        _load().orc_gemm_all(ctypes.byref(s), self._ptr(A), self._ptr(B), self._ptr(C),
-                             pre.ctypes.data, post.ctypes.data, nthreads)
+        _check(_load().orc_gemm_all(ctypes.byref(s), self._ptr(A), self._ptr(B), self._ptr(C),
+                             pre.ctypes.data, post.ctypes.data, nthreads))
         return pre, post
 
 
@@ -255,8 +273,11 @@ def problem_from(inp, act=None, alpha=None, beta=None):
         c_n = C.stride(2) == 1
         kw = dict(c_dt=inp.c_dt, c_nmajor=c_n, ldc=C.stride(1) if c_n else C.stride(2),
                   sc=0 if varlen else C.stride(0))
+    a_rows = None
+    if a_idx is not None:  # the rows (varlen-M) or columns (varlen-K) an index may name
+        a_rows = A.shape[0] if varlen else A.shape[1]
     return Problem(inp.M, inp.N, inp.K, L, inp.a_dt, inp.b_dt, a_kmajor=a_k, b_kmajor=b_k,
-                   lda=lda, ldb=ldb, sa=sa, sb=sb,
+                   lda=lda, ldb=ldb, sa=sa, sb=sb, a_rows=a_rows,
                    alpha=inp.alpha if alpha is None else alpha,
                    beta=inp.beta if beta is None else beta,
                    act=inp.act if act is None else act, cu_seqlens=inp.cu_seqlens,

@@ -227,7 +227,14 @@ double orc_dact(int act, double x) {
  * group l sums k over [cu_k[l], cu_k[l+1]), an empty range giving acc = 0.
  * Gathered A (mAIdx on the same pages; the gather copies of load_AB_gather_A and
  * _make_gather_A_copy): with varlen-M, the A row read for global output row m is
- * a_idx[m]; with varlen-K, the A column read for global k is a_idx[k]. */
+ * a_idx[m]; with varlen-K, the A column read for global k is a_idx[k]. The pages load only
+ * rows that exist and leave the rest of the tile empty; the reading taken here is that an
+ * index outside [0, a_rows) (a_rows = the rows, or columns, of A an index may name) reads
+ * a zero row (column), i.e. contributes nothing to the sum.
+ * Preconditions, checked by every entry point below (they return ORC_ERR_* instead of
+ * reading out of bounds): cu_seqlens starts at 0, never decreases and ends at M (every
+ * global row belongs to exactly one group); cu_seqlens_k starts at 0, never decreases and
+ * ends at most at K; requested (l, m, n) lie inside the output. */
 typedef struct {
   int64_t M, N, K, L;
   int32_t a_dt, b_dt, c_dt;
@@ -243,7 +250,30 @@ typedef struct {
   int32_t varlen_k;          /* 1: grouped K, cu_seqlens_k given */
   const int32_t* cu_seqlens_k; /* host array, L+1 entries, when varlen_k */
   const int32_t* a_idx;      /* host array or NULL: gathered A rows (varlen-M) / columns (varlen-K) */
+  int64_t a_rows;            /* with a_idx: the rows (varlen-M) / columns (varlen-K) of A it may name */
 } orc_problem;
+
+enum { ORC_OK = 0, ORC_ERR_CU_SEQLENS = -1, ORC_ERR_CU_SEQLENS_K = -2, ORC_ERR_INDEX = -3 };
+
+/* The preconditions above; ORC_OK or the first one violated. */
+static int validate(const orc_problem* p) {
+  if (p->varlen) {
+    if (p->cu_seqlens[0] != 0 || p->cu_seqlens[p->L] != p->M) return ORC_ERR_CU_SEQLENS;
+    for (int64_t g = 0; g < p->L; ++g)
+      if (p->cu_seqlens[g + 1] < p->cu_seqlens[g]) return ORC_ERR_CU_SEQLENS;
+  }
+  if (p->varlen_k) {
+    if (p->cu_seqlens_k[0] != 0 || p->cu_seqlens_k[p->L] > p->K) return ORC_ERR_CU_SEQLENS_K;
+    for (int64_t g = 0; g < p->L; ++g)
+      if (p->cu_seqlens_k[g + 1] < p->cu_seqlens_k[g]) return ORC_ERR_CU_SEQLENS_K;
+  }
+  return ORC_OK;
+}
+
+static int point_ok(const orc_problem* p, int64_t l, int64_t m, int64_t n) {
+  const int64_t nb = p->varlen ? 1 : p->L;
+  return l >= 0 && l < nb && m >= 0 && m < p->M && n >= 0 && n < p->N;
+}
 
 static double load_elem(const void* base, int dt, int64_t idx) {
   switch (dt) {
@@ -256,7 +286,8 @@ static double load_elem(const void* base, int dt, int64_t idx) {
   }
 }
 
-/* Group owning global row r (plain linear search); -1 if none. */
+/* Group owning global row r (plain linear search). validate() guarantees one exists for
+ * every r in [0, M). */
 static int64_t group_of_row(const orc_problem* p, int64_t r) {
   for (int64_t g = 0; g < p->L; ++g)
     if (r >= p->cu_seqlens[g] && r < p->cu_seqlens[g + 1]) return g;
@@ -284,9 +315,11 @@ static void elem(const orc_problem* p, const void* A, const void* B, const void*
     la = lb = 0;
   }
   int64_t ma = (p->a_idx && p->varlen) ? (int64_t)p->a_idx[m] : m; /* the A row read */
+  const int row_zero = p->a_idx && p->varlen && (ma < 0 || ma >= p->a_rows);
   double acc = 0.0;
-  for (int64_t k = k_lo; k < k_hi; ++k) {
+  for (int64_t k = k_lo; k < k_hi && !row_zero; ++k) {
     int64_t ka = (p->a_idx && p->varlen_k) ? (int64_t)p->a_idx[k] : k; /* the A column read */
+    if (p->a_idx && p->varlen_k && (ka < 0 || ka >= p->a_rows)) continue; /* a zero column */
     int64_t ia = la * p->sa + (p->a_kmajor ? ma * p->lda + ka : ka * p->lda + ma);
     int64_t ib = lb * p->sb + (p->b_kmajor ? n * p->ldb + k : k * p->ldb + n);
     acc += load_elem(A, p->a_dt, ia) * load_elem(B, p->b_dt, ib);
@@ -362,6 +395,10 @@ static void parallel(job_t base, int64_t count, int nthreads, void* (*fn)(void*)
 /* Output elements at the given (l, m, n) triples (varlen: l ignored, m = global row). */
 int orc_gemm_points(const orc_problem* p, const void* A, const void* B, const void* C,
                     int64_t npts, const int64_t* pts, double* pre, double* post, int nthreads) {
+  int rc = validate(p);
+  if (rc != ORC_OK) return rc;
+  for (int64_t i = 0; i < npts; ++i)
+    if (!point_ok(p, pts[3 * i], pts[3 * i + 1], pts[3 * i + 2])) return ORC_ERR_INDEX;
   job_t j;
   memset(&j, 0, sizeof(j));
   j.p = p; j.A = A; j.B = B; j.C = C; j.npts = npts; j.pts = pts; j.pre = pre; j.post = post;
@@ -372,6 +409,10 @@ int orc_gemm_points(const orc_problem* p, const void* A, const void* B, const vo
 /* Whole output rows (l, m): pre/post are [nrows][N]. */
 int orc_gemm_rows(const orc_problem* p, const void* A, const void* B, const void* C,
                   int64_t nrows, const int64_t* rows, double* pre, double* post, int nthreads) {
+  int rc = validate(p);
+  if (rc != ORC_OK) return rc;
+  for (int64_t i = 0; i < nrows; ++i)
+    if (p->N > 0 && !point_ok(p, rows[2 * i], rows[2 * i + 1], 0)) return ORC_ERR_INDEX;
   job_t j;
   memset(&j, 0, sizeof(j));
   j.p = p; j.A = A; j.B = B; j.C = C; j.nrows = nrows; j.rows = rows; j.pre = pre; j.post = post;
@@ -573,10 +614,15 @@ uint64_t orc_fdm_random(uint64_t count, uint64_t seed) {
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull; z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     z ^= z >> 31;
     uint32_t n = (uint32_t)(z & 0x7FFFFFFFu);
-    /* log-uniform divisor so that small and large divisors are both frequent */
+    /* log-uniform divisor (so that small and large ones are both frequent), even or odd:
+     * a second draw gives d in [2^(bits-1), 2^bits) for bits in 1..31 */
     uint32_t bits = (uint32_t)((z >> 32) % 31) + 1;
-    uint32_t d = (uint32_t)((z >> 40) | 1u) & ((bits >= 31) ? 0x7FFFFFFFu : ((1u << bits) - 1u));
-    if (d == 0) d = 1;
+    uint64_t z2;
+    s += 0x9E3779B97F4A7C15ull; z2 = s;
+    z2 = (z2 ^ (z2 >> 30)) * 0xBF58476D1CE4E5B9ull; z2 = (z2 ^ (z2 >> 27)) * 0x94D049BB133111EBull;
+    z2 ^= z2 >> 31;
+    uint32_t top = 1u << (bits - 1);
+    uint32_t d = top | ((uint32_t)z2 & (top - 1u));
     uint32_t mult, shift, q, r;
     orc_fdm_create(d, &mult, &shift);
     orc_fdm_divmod(n, d, mult, shift, &q, &r);
