@@ -87,3 +87,40 @@ def gather(arr, pts, varlen):
     if varlen:
         return arr[pts[:, 1], pts[:, 2]]
     return arr[pts[:, 0], pts[:, 1], pts[:, 2]]
+
+
+def _m_blocks(inp, TM):
+    """(l, first row, rows) of every M-block of the output: per batch, or per group (varlen)."""
+    if inp.varlen:
+        cu = inp.cu_seqlens
+        return [(0, int(cu[g]) + b, min(TM, int(cu[g + 1]) - int(cu[g]) - b))
+                for g in range(len(cu) - 1) for b in range(0, int(cu[g + 1]) - int(cu[g]), TM)]
+    return [(l, b, min(TM, inp.M - b)) for l in range(inp.L) for b in range(0, inp.M, TM)]
+
+
+def tile_cover_points(inp, TM, TN, seed, rows_split=2, cols_split=4):
+    """Deterministic sample that touches every output tile: for each TM x TN tile, one point
+    in each cell of a rows_split x cols_split grid over it (the wave sub-tiles of both the
+    4-wave 2 x 2 and the 8-wave 2 x 4 layouts), drawn at a seeded position inside the cell
+    and clipped to the output. Returns (l, m, n) triples (varlen: m is the global row)."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    pts = []
+    for l, m0, mr in _m_blocks(inp, TM):
+        for n0 in range(0, inp.N, TN):
+            nr = min(TN, inp.N - n0)
+            for i in range(rows_split):
+                for j in range(cols_split):
+                    lo_m, lo_n = i * TM // rows_split, j * TN // cols_split
+                    if lo_m >= mr or lo_n >= nr:
+                        continue
+                    hi_m = min(mr, (i + 1) * TM // rows_split)
+                    hi_n = min(nr, (j + 1) * TN // cols_split)
+                    pts.append((l, m0 + int(r.integers(lo_m, hi_m)), n0 + int(r.integers(lo_n, hi_n))))
+    return np.array(pts, dtype=np.int64).reshape(-1, 3)
+
+
+def tile_rows(inp, TM, seed):
+    """One whole output row per M-block (a seeded row inside it): (l, m) pairs."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    return np.array([(l, m0 + int(r.integers(0, mr))) for l, m0, mr in _m_blocks(inp, TM)],
+                    dtype=np.int64).reshape(-1, 2)

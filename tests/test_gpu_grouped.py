@@ -256,12 +256,12 @@ def test_gather_k_dynamic_equals_static():
 # ---------------------------------------------------------------------------------------
 
 def test_workload_varlen_k_moe():
-    full_size(W.varlen_k_moe(), npts=2000, rows=1)
+    full_size(W.varlen_k_moe())
 
 
 def test_workload_varlen_moe_gather():
-    full_size(W.varlen_moe_gather(), npts=2000, rows=2)
+    full_size(W.varlen_moe_gather(), every_tile_row=True)
 
 
 def test_workload_varlen_k_moe_gather():
-    full_size(W.varlen_k_moe_gather(), npts=2000, rows=1)
+    full_size(W.varlen_k_moe_gather())

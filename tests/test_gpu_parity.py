@@ -14,7 +14,7 @@ import torch
 import oracle
 import workloads as W
 from parity import (check_close, gather, oracle_codes, out_like, problem_of, run_hip,
-                    sample_points, to_dev, tol_for)
+                    sample_points, tile_cover_points, tile_rows, to_dev, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -512,22 +512,25 @@ def test_fastdivmod_device_exhaustive_below_2_16():
 # the five workloads at full size (sampled outputs) and the guards that isolate the GEMM
 # ---------------------------------------------------------------------------------------
 
-def full_size(inp, npts=3000, rows=2, seed=0, **kw):
+def full_size(inp, seed=0, every_tile_row=False, **kw):
+    """Full-size run checked on a deterministic sample that touches every output tile (one
+    point per wave sub-tile of each tile, plus the output's corners) and on whole rows: one
+    per M-block with every_tile_row, else two."""
     announce(f"{inp.name} full size")
-    d, p, _ = run_hip(inp, **kw)
+    d, p, plan = run_hip(inp, **kw)
+    TM, TN = plan.grid()[:2]
     prob = problem_of(inp)
     codes = oracle_codes(inp)
-    pts = sample_points(inp, npts, seed)
+    pts = np.concatenate([tile_cover_points(inp, TM, TN, seed), sample_points(inp, 0, seed)])
     pre, post = prob.points(*codes, pts)
     tol, rms = tol_for(inp)
     if d is not None:
         check_close(gather(d, pts, inp.varlen), pre, tol, rms, "D sampled")
     if p is not None:
         check_close(gather(p, pts, inp.varlen), post, tol, rms, "PostAct sampled")
-    # whole rows (every column of a few rows, across all N-tiles)
-    r = np.random.Generator(np.random.PCG64(seed + 1))
-    L = 1 if inp.varlen else inp.L
-    rr = np.stack([r.integers(0, L, rows), r.integers(0, inp.M, rows)], 1)
+    rr = tile_rows(inp, TM, seed + 1)
+    if not every_tile_row:
+        rr = rr[np.random.Generator(np.random.PCG64(seed + 2)).choice(len(rr), size=min(2, len(rr)), replace=False)]
     rpre, rpost = prob.rows(*codes, rr)
     for i, (l, m) in enumerate(rr):
         if d is not None:
@@ -555,25 +558,25 @@ def test_workload_act_4096_gemm_only_guard():
 
 
 def test_workload_square_8192_f16():
-    full_size(W.square_8192("f16"), npts=1500, rows=1)
+    full_size(W.square_8192("f16"), every_tile_row=True)
 
 
 def test_workload_square_8192_bf16():
-    full_size(W.square_8192("bf16"), npts=1500, rows=1)
+    full_size(W.square_8192("bf16"), every_tile_row=True)
 
 
 def test_workload_batched_2048():
-    full_size(W.batched_2048(), npts=2000, rows=2)
+    full_size(W.batched_2048())
 
 
 def test_workload_fp8_8192():
-    full_size(W.fp8_8192(), npts=1500, rows=1)
+    full_size(W.fp8_8192(), every_tile_row=True)
 
 
 def test_workload_varlen_moe():
-    full_size(W.varlen_moe(), npts=3000, rows=2)
+    full_size(W.varlen_moe(), every_tile_row=True)
 
 
 def test_workload_varlen_moe_unscaled_guard():
     # N(0,1) inputs: SiLU of O(64) values, far from the all-zero output
-    full_size(W.varlen_moe(std=1.0), npts=2000, rows=1)
+    full_size(W.varlen_moe(std=1.0))
