@@ -198,6 +198,15 @@ class Plan:
             st = self._lib.gemm_run(*args, _stream(stream))
         _abi.check(st)
 
+    def run_noalloc(self, A, B, C=None, D=None, PostAct=None, alpha_dev=None, beta_dev=None,
+                    cu_seqlens_m=None, stream=None):
+        """Enqueue with the dynamic schedule on the library's own per-device counters
+        (gemm_run_dynamic_noalloc): no device memory is allocated by the call. Calls that
+        may overlap on one GPU race on those counters."""
+        _abi.check(self._lib.gemm_run_dynamic_noalloc(self.handle, _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                                      _ptr(PostAct), _ptr(alpha_dev), _ptr(beta_dev),
+                                                      _ptr(cu_seqlens_m), _stream(stream)))
+
     def grid(self, num_cus=None):
         """(tile_m, tile_n, group_m, xcd_remap, tiles, grid) for a device with num_cus CUs."""
         if num_cus is None:

@@ -145,6 +145,44 @@ __global__ __launch_bounds__(256) void fastdivmod_check_kernel(uint32_t d_lo, ui
   if (local) atomicAdd(bad, local);
 }
 
+// ---- the dynamic schedule's queue counters for callers that cannot allocate
+// (gemm_run_dynamic_noalloc): one array per device, held for the life of the process. Only
+// its first kQueueCounters entries are used (one counter per XCD queue); the rest is slack.
+constexpr int kQueueCounters = 8;
+constexpr int kScratchInts = 64;  // 256 bytes
+static_assert(kQueueCounters <= kScratchInts, "the queue counters must fit the scratch array");
+static __device__ __align__(256) int32_t scratch[kScratchInts];
+
+// Device address of `scratch` on each device, looked up once with that device current.
+// (In host code the array's name is only a host-side stand-in, never a device address.)
+constexpr int kMaxDevices = 64;
+static std::atomic<int32_t*> g_scratch_ptr[kMaxDevices];
+
+static gemm_status scratch_of_current_device(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GEMM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GEMM_ERR_UNSUPPORTED, "gemm_run_dynamic_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+  int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !addr)
+      return fail(GEMM_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    p = (int32_t*)addr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);  // (a racing lookup stores the same value)
+  }
+  *out = p;
+  return GEMM_OK;
+}
+
+// Zero the counters with a vector store (a fill kernel rather than hipMemsetAsync, so that
+// the call can sit in a captured graph).
+__global__ __launch_bounds__(64) void zero_counters_kernel(int32_t* c, int n) {
+  if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
+}
+
 // The entry points of the C ABI that predate varlen-K and gathered A take no place for their
 // device arrays: such plans must go through gemm_run_ex.
 static gemm_status legacy_ok(const gemm_plan* plan, const char* fn) {
@@ -185,6 +223,23 @@ gemm_status gemm_run_dynamic(const gemm_plan* plan, const void* A, const void* B
   if (gep::legacy_ok(plan, "gemm_run_dynamic") != GEMM_OK) return GEMM_ERR_INVALID_ARG;
   return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, tile_counters,
                        tile_log, max_iters, stream);
+}
+
+gemm_status gemm_run_dynamic_noalloc(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
+                                     void* PostAct, const float* alpha_dev, const float* beta_dev,
+                                     const int32_t* cu_seqlens_m, void* stream) {
+  if (gep::legacy_ok(plan, "gemm_run_dynamic_noalloc") != GEMM_OK) return GEMM_ERR_INVALID_ARG;
+  if (!plan) return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_run_dynamic_noalloc: NULL plan");
+  int32_t* ctr = nullptr;
+  gemm_status st = gep::scratch_of_current_device(&ctr);
+  if (st != GEMM_OK) return st;
+  // the counters start every call at zero (each call also leaves them at zero)
+  hipLaunchKernelGGL(gep::zero_counters_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, ctr,
+                     gep::kQueueCounters);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return gep::fail(GEMM_ERR_HIP, "counter reset launch: %s", hipGetErrorString(e));
+  return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, ctr, nullptr, 0,
+                       stream);
 }
 
 gemm_status gemm_run_logged(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,

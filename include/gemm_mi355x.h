@@ -257,6 +257,22 @@ gemm_status gemm_run_dynamic(const gemm_plan* plan, const void* A, const void* B
                              const int32_t* cu_seqlens_m, int32_t* tile_counters, int32_t* tile_log,
                              int32_t max_iters, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): gemm_run_dynamic without the
+ * tile_counters argument (and without a tile log). The queue counters live in a 256-byte
+ * array of the library's own device memory, one per GPU, held until the process ends; the
+ * dynamic schedule uses 8 int32 of it at any problem size, so no size is rejected for
+ * scratch. Each call first zeroes those counters with a one-workgroup fill kernel on
+ * `stream`, then launches exactly as gemm_run_dynamic; results equal gemm_run's bit for bit.
+ * No hipMalloc, hipFree or other allocating call is made. Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (other streams, other threads) race on it
+ * and must be serialised by the caller. The first call on a device looks the array's
+ * address up (hipGetSymbolAddress) with that device current. Returns as gemm_run_dynamic
+ * (INVALID_ARG for varlen-K and gathered-A plans), UNSUPPORTED on a device index >= 64. */
+gemm_status gemm_run_dynamic_noalloc(const gemm_plan* plan, const void* A, const void* B, const void* C,
+                                     void* D, void* PostAct, const float* alpha_dev,
+                                     const float* beta_dev, const int32_t* cu_seqlens_m, void* stream);
+
 /* Release a plan (NULL is accepted). */
 gemm_status gemm_destroy(gemm_plan* plan);
 
