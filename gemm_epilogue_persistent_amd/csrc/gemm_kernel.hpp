@@ -622,7 +622,31 @@ struct GemmKernel {
     ti.b_tile = (const char*)p.B + b_off;
     ti.a_room = p.a_bytes - a_off;
     ti.b_room = p.b_bytes - b_off;
+    // Everything above is the same in every lane, but grouped tiles derive it from LDS and
+    // global loads (the group table, cu_seqlens), whose results the compiler keeps per lane:
+    // the buffer descriptors of every k-tile were then rebuilt with 64-bit vector adds and
+    // readfirstlane in the main loop. Stating uniformity here keeps the tile in SGPRs.
+    if constexpr (VARLEN || VARK) {
+      ti.l = uni(ti.l);
+      ti.m0 = uni(ti.m0);
+      ti.n0 = uni(ti.n0);
+      ti.row_end = uni(ti.row_end);
+      ti.klen = uni(ti.klen);
+      ti.kb = uni(ti.kb);
+      ti.mb = uni(ti.mb);
+      ti.nb = uni(ti.nb);
+      ti.a_tile = (const char*)uni64((int64_t)ti.a_tile);
+      ti.b_tile = (const char*)uni64((int64_t)ti.b_tile);
+      ti.a_room = uni64(ti.a_room);
+      ti.b_room = uni64(ti.b_room);
+    }
     return ti;
+  }
+  static __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+  static __device__ __forceinline__ int64_t uni64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
   }
 
   // Buffer resources of k-tile j of the current tile (k-tiles past the end read as zero).
@@ -1207,7 +1231,7 @@ struct GemmKernel {
     GEP_LDS char* smem = (GEP_LDS char*)smem_raw;
     // the dynamic schedule's next queue position, published by thread 0
     volatile int32_t* next_slot = (volatile int32_t*)(smem_raw + kLdsBytes);
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, lane_id = lane;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     if constexpr (NW == 8) {
       // With two waves per SIMD a wave has 256 registers in all. An explicit AGPR operand
@@ -1308,6 +1332,10 @@ struct GemmKernel {
     // a tile's first k-tile goes into the staging registers as early as possible
     auto begin_tile = [&](int t) {
       ti = decode(p, t, gstart, t_lo);
+      // the loaders' lane offsets are recomputed here from an opaque copy of the lane id: hoisted
+      // out of the tile loop they stay live across the main loop and spill
+      int lane = lane_id;
+      asm volatile("" : "+v"(lane));
       if constexpr (GAK) la.init_gather_k(wave, lane, ti.row_end - ti.m0, ti.klen);
       else if constexpr (GA) la.init_gather(wave, lane, ti.row_end - ti.m0, p.lda * kES, ti.klen, p.a_idx + ti.m0, p.a_rows);
       else la.init(wave, lane, ti.row_end - ti.m0, p.lda * kES, ti.klen);
