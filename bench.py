@@ -39,7 +39,7 @@ def source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemm_epilogue_persistent_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".cpp")) and f != "probe.hip":  # the probe is not the GEMM
+        if f.endswith((".hip", ".hpp", ".cpp")):
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -178,12 +178,12 @@ def time_plan(plan, args, steps, warmup, settle_s=0.0):
 
 
 def mfma_ceiling(dtype, peak, reps=3):
-    """The library's MFMA rate probe: pure MFMA loops on uniform [-1, 1) operands held in
+    """The MFMA rate probe (gemm_epilogue_persistent_amd.measure): pure MFMA loops on uniform [-1, 1) operands held in
     registers, one 4-wave workgroup per CU, no memory traffic. Returns the sustained rate and
     the shader clock it ran at (cycles over the 100 MHz real-time counter)."""
     import statistics
     import torch
-    from gemm_epilogue_persistent_amd import probe_mfma
+    from gemm_epilogue_persistent_amd.measure import probe_mfma
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
     iters = 20000 if dtype == "bf16" else 10000

@@ -27,7 +27,7 @@ _TORCH_DT = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32",
              torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}
 
 __all__ = ["Plan", "gemm", "gemm_dact", "gemm_create", "gemm_run", "plan_grid", "configs", "tune", "fastdivmod_params",
-           "fastdivmod_check", "probe_mfma", "GemmError", "library_path"]
+           "fastdivmod_check", "GemmError", "library_path"]
 
 
 def library_path():
@@ -297,11 +297,3 @@ def fastdivmod_check(d_lo, d_hi, n_count, bad_dev, stream=None):
     """Enqueue the device FastDivmod self-check; adds mismatches to bad_dev (uint64)."""
     lib = _abi.load()
     _abi.check(lib.gemm_fastdivmod_check(d_lo, d_hi, n_count, _ptr(bad_dev), _stream(stream)))
-
-
-def probe_mfma(dtype, iters, seed, blocks, out_dev, stream=None):
-    """Launch the library's MFMA rate probe (see gemm_probe_mfma): out_dev is a device int64
-    tensor of 2 * blocks elements receiving {shader cycles, 100 MHz ticks} per workgroup."""
-    lib = _abi.load()
-    _abi.check(lib.gemm_probe_mfma(DT[dtype], int(iters), int(seed) & 0xFFFFFFFF, int(blocks), _ptr(out_dev),
-                                   _stream(stream)))

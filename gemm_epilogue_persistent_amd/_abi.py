@@ -78,8 +78,6 @@ def load():
         lib.gemm_fastdivmod_params.argtypes = [u32, ctypes.POINTER(u32), ctypes.POINTER(u32)]
         lib.gemm_fastdivmod_check.restype = ctypes.c_int
         lib.gemm_fastdivmod_check.argtypes = [u32, u32, u32, vp, vp]
-        lib.gemm_probe_mfma.restype = ctypes.c_int
-        lib.gemm_probe_mfma.argtypes = [i32, i32, u32, i32, vp, vp]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_status_string.argtypes = [ctypes.c_int]
         lib.gemm_last_error.restype = ctypes.c_char_p

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgemm_mi355x.so")
 # one unit per (operand type, epilogue kind, varlen mode) family of kernels
-UNITS = ["plan.cpp", "gemm_api.hip", "probe.hip"] + [
+UNITS = ["plan.cpp", "gemm_api.hip"] + [
     f"inst_{op}_{fam}.hip" for op in ("f16", "bf16", "fp8") for fam in ("fwd", "vm", "vk", "dact", "dact_vm")]
 
 
@@ -34,9 +34,13 @@ def flags():
             "-Wno-unused-command-line-argument"]
 
 
+PROBE_SRC = os.path.join(HERE, "measure", "mfma_probe.hip")
+PROBE_LIB = os.path.join(HERE, "measure", "libmfma_probe.so")
+
+
 def _compile(unit, verbose):
-    src = os.path.join(CSRC, unit)
-    obj = os.path.join(BUILD, unit + ".o")
+    src = os.path.join(CSRC, unit) if not os.path.isabs(unit) else unit
+    obj = os.path.join(BUILD, os.path.basename(unit) + ".o")
     cmd = [hipcc()] + flags() + ["-c", src, "-o", obj]
     if unit.endswith(".cpp"):  # host-only C++ (no HIP call, no device code)
         cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", src, "-o", obj]
@@ -52,13 +56,16 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(len(UNITS), os.cpu_count() or 1, 16)
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda u: _compile(u, verbose), UNITS))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+        objs = list(ex.map(lambda u: _compile(u, verbose), UNITS + [PROBE_SRC]))
+    probe_obj = objs.pop()
+    # the GEMM library, and the benchmark's MFMA probe in a library of its own
+    for lib, parts in ((LIB, objs), (PROBE_LIB, [probe_obj])):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + parts
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -1,17 +1,15 @@
-// MFMA rate probe (measurement support for the roofline): one workgroup of 4 waves per
-// compute unit issues back-to-back independent MFMAs on full-entropy operands in registers,
-// with no memory traffic, and records its shader-clock and real-time cycle counts. On a
+// MFMA rate probe: measurement support for the benchmark's roofline, built into its own
+// library (libmfma_probe.so), apart from the GEMM library. One workgroup of 4 waves per compute
+// unit issues back-to-back independent MFMAs on full-entropy operands in registers, with no
+// memory traffic, and records its shader-clock and real-time cycle counts. On a
 // power-limited part the rate such a loop sustains with random operands is the practical
 // ceiling of any GEMM kernel on the same data; the clock it settles at is reported with it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/gemm_mi355x.h"
-#include "params.hpp"
+namespace probe {
 
-namespace gep {
-gemm_status fail(gemm_status st, const char* fmt, ...);
-void clear_error();
+enum { OP_BF16 = 0, OP_FP8 = 1 };  // the dtype codes of mfma_probe_run
 
 typedef __bf16 pbf16x8 __attribute__((ext_vector_type(8)));
 typedef float pf32x16 __attribute__((ext_vector_type(16)));
@@ -82,21 +80,22 @@ __global__ __launch_bounds__(256, 1) void mfma_probe_kernel(int iters, uint32_t 
   if (sum == 1.2345e-30f) out[0] = -1;  // keeps the accumulators live
 }
 
-}  // namespace gep
+}  // namespace probe
 
-extern "C" gemm_status gemm_probe_mfma(int32_t dtype, int32_t iters, uint32_t seed, int32_t blocks, int64_t* out_dev,
-                                       void* stream) {
-  if (iters <= 0 || blocks <= 0 || !out_dev)
-    return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_probe_mfma: iters, blocks > 0 and an output buffer required");
-  if (dtype != GEMM_DT_BF16 && dtype != GEMM_DT_E4M3)
-    return gep::fail(GEMM_ERR_UNSUPPORTED, "gemm_probe_mfma: dtype must be bf16 or e4m3");
+// Launch `blocks` workgroups of 4 waves, each wave issuing iters x 16 independent MFMAs
+// (dtype 0: v_mfma_f32_32x32x16_bf16; 1: the 32x32x64 fp8 form, e4m3 operands) on uniform
+// [-1, 1) operands drawn in registers from `seed`. Workgroup b writes int64 {shader-clock
+// cycles, 100 MHz real-time ticks} of its loop to out_dev[2b], out_dev[2b+1] (a device buffer
+// of 2 * blocks int64, owned by the caller). Asynchronous on `stream`. Returns 0 on success,
+// 1 for a bad argument (iters or blocks <= 0, NULL buffer, unknown dtype), 2 if the launch
+// fails.
+extern "C" int mfma_probe_run(int32_t dtype, int32_t iters, uint32_t seed, int32_t blocks, int64_t* out_dev,
+                              void* stream) {
+  if (iters <= 0 || blocks <= 0 || !out_dev || (dtype != probe::OP_BF16 && dtype != probe::OP_FP8)) return 1;
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == GEMM_DT_BF16)
-    hipLaunchKernelGGL(gep::mfma_probe_kernel<gep::OP_BF16>, dim3(blocks), dim3(256), 0, s, iters, seed, out_dev);
+  if (dtype == probe::OP_BF16)
+    hipLaunchKernelGGL(probe::mfma_probe_kernel<probe::OP_BF16>, dim3(blocks), dim3(256), 0, s, iters, seed, out_dev);
   else
-    hipLaunchKernelGGL(gep::mfma_probe_kernel<gep::OP_FP8>, dim3(blocks), dim3(256), 0, s, iters, seed, out_dev);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return gep::fail(GEMM_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
-  gep::clear_error();
-  return GEMM_OK;
+    hipLaunchKernelGGL(probe::mfma_probe_kernel<probe::OP_FP8>, dim3(blocks), dim3(256), 0, s, iters, seed, out_dev);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }

@@ -311,17 +311,6 @@ gemm_status gemm_fastdivmod_params(uint32_t d, uint32_t* multiplier, uint32_t* s
 gemm_status gemm_fastdivmod_check(uint32_t d_lo, uint32_t d_hi, uint32_t n_count,
                                   unsigned long long* bad_dev, void* stream);
 
-/* Measurement support, not part of the GEMM: launch `blocks` workgroups of 4 waves, each
- * wave issuing iters x 16 independent MFMAs (dtype GEMM_DT_BF16: v_mfma_f32_32x32x16_bf16;
- * GEMM_DT_E4M3: the 32x32x64 fp8 form) on uniform [-1, 1) operands drawn in registers from
- * `seed`, with no memory traffic. Workgroup b writes int64 {shader-clock cycles, 100 MHz
- * real-time ticks} of its loop to out_dev[2b], out_dev[2b+1] (device buffer of 2 * blocks
- * int64, caller-owned). With one workgroup per CU this measures the MFMA rate and clock
- * the chip sustains on full-entropy data under its power limit. Asynchronous on `stream`;
- * INVALID_ARG for iters or blocks <= 0 or a NULL buffer, UNSUPPORTED for another dtype. */
-gemm_status gemm_probe_mfma(int32_t dtype, int32_t iters, uint32_t seed, int32_t blocks, int64_t* out_dev,
-                            void* stream);
-
 /* Static description of a status code (never NULL). */
 const char* gemm_status_string(gemm_status status);
 
