@@ -27,7 +27,7 @@ _TORCH_DT = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32",
              torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}
 
 __all__ = ["Plan", "gemm", "gemm_dact", "gemm_create", "gemm_run", "plan_grid", "configs", "tune", "fastdivmod_params",
-           "fastdivmod_check", "GemmError", "library_path"]
+           "fastdivmod_check", "check_cu_seqlens", "GemmError", "library_path"]
 
 
 def library_path():
@@ -297,3 +297,14 @@ def fastdivmod_check(d_lo, d_hi, n_count, bad_dev, stream=None):
     """Enqueue the device FastDivmod self-check; adds mismatches to bad_dev (uint64)."""
     lib = _abi.load()
     _abi.check(lib.gemm_fastdivmod_check(d_lo, d_hi, n_count, _ptr(bad_dev), _stream(stream)))
+
+
+def check_cu_seqlens(cu, total, exact_end=True, stream=None):
+    """Enqueue the library's cu_seqlens check (gemm_check_cu_seqlens) and return a one-element
+    int32 device tensor: 0 if valid, else 1 + the index of the first bad entry."""
+    if cu.dtype != torch.int32 or not cu.is_cuda or not cu.is_contiguous():
+        raise ValueError("cu: contiguous int32 device tensor expected")
+    status = torch.empty(1, dtype=torch.int32, device=cu.device)
+    _abi.check(_abi.load().gemm_check_cu_seqlens(_ptr(cu), cu.numel() - 1, int(total), int(bool(exact_end)),
+                                                 _ptr(status), _stream(stream)))
+    return status

@@ -64,6 +64,8 @@ def load():
         lib.gemm_run_dynamic.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
         lib.gemm_run_dynamic_noalloc.restype = ctypes.c_int
         lib.gemm_run_dynamic_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.gemm_check_cu_seqlens.restype = ctypes.c_int
+        lib.gemm_check_cu_seqlens.argtypes = [vp, i32, i32, i32, vp, vp]
         lib.gemm_run_ex.restype = ctypes.c_int
         lib.gemm_run_ex.argtypes = [vp, ctypes.POINTER(GemmArgs), vp]
         lib.gemm_destroy.restype = ctypes.c_int

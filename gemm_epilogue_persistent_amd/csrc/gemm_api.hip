@@ -183,6 +183,22 @@ __global__ __launch_bounds__(64) void zero_counters_kernel(int32_t* c, int n) {
   if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
 }
 
+// cu_seqlens check: one workgroup; *status = 0 when cu[0] == 0, cu never decreases and cu[L]
+// is total (exact_end) or at most total; else 1 + the index of the first offending entry.
+__global__ __launch_bounds__(256) void check_cu_seqlens_kernel(const int32_t* cu, int32_t L, int32_t total,
+                                                               int32_t exact_end, int32_t* status) {
+  __shared__ int32_t first;
+  if (threadIdx.x == 0) first = 0x7FFFFFFF;
+  __syncthreads();
+  for (int32_t i = threadIdx.x; i <= L; i += blockDim.x) {
+    const int32_t v = cu[i];
+    const bool ok = (i == 0 ? v == 0 : v >= cu[i - 1]) && (i < L || (exact_end ? v == total : v <= total));
+    if (!ok) atomicMin(&first, i);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *status = first == 0x7FFFFFFF ? 0 : first + 1;
+}
+
 // The entry points of the C ABI that predate varlen-K and gathered A take no place for their
 // device arrays: such plans must go through gemm_run_ex.
 static gemm_status legacy_ok(const gemm_plan* plan, const char* fn) {
@@ -240,6 +256,20 @@ gemm_status gemm_run_dynamic_noalloc(const gemm_plan* plan, const void* A, const
   if (e != hipSuccess) return gep::fail(GEMM_ERR_HIP, "counter reset launch: %s", hipGetErrorString(e));
   return gep::run_impl(plan, A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, nullptr, ctr, nullptr, 0,
                        stream);
+}
+
+gemm_status gemm_check_cu_seqlens(const int32_t* cu_seqlens, int32_t L, int32_t total, int32_t exact_end,
+                                  int32_t* status_dev, void* stream) {
+  if (!cu_seqlens || !status_dev || L < 0 || total < 0 || (exact_end != 0 && exact_end != 1))
+    return gep::fail(GEMM_ERR_INVALID_ARG, "gemm_check_cu_seqlens: NULL array or status, L < 0, total < 0 or bad mode");
+  if (((uintptr_t)cu_seqlens & 3u) != 0 || ((uintptr_t)status_dev & 3u) != 0)
+    return gep::fail(GEMM_ERR_ALIGNMENT, "gemm_check_cu_seqlens: arrays must be 4-byte aligned");
+  hipLaunchKernelGGL(gep::check_cu_seqlens_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, cu_seqlens, L, total,
+                     exact_end, status_dev);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return gep::fail(GEMM_ERR_HIP, "cu_seqlens check launch: %s", hipGetErrorString(e));
+  gep::clear_error();
+  return GEMM_OK;
 }
 
 gemm_status gemm_run_logged(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,

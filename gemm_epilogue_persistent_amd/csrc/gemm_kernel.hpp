@@ -1268,17 +1268,23 @@ struct GemmKernel {
       constexpr int kPer = (kMaxVarlenGroups + kThreads - 1) / kThreads;
       int32_t local[kPer];
       int32_t sum = 0;
+      // cu_seqlens must start at 0, never decrease and end at M; otherwise no tile is run and
+      // nothing is written (a decreasing or overlong array would address rows outside D)
+      int bad = 0;
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int g = tid * kPer + q;
         int32_t tiles = 0;
         if (g < G) {
-          const int rows = p.cu_seqlens[g + 1] - p.cu_seqlens[g];
-          tiles = ((rows + MT - 1) / MT) * p.tn;
+          const int c0 = p.cu_seqlens[g], c1 = p.cu_seqlens[g + 1];
+          const int rows = c1 - c0;
+          bad |= rows < 0 || (g == 0 && c0 != 0) || (g == G - 1 && c1 != p.M);
+          tiles = rows > 0 ? ((rows + MT - 1) / MT) * p.tn : 0;
         }
         local[q] = sum;
         sum += tiles;
       }
+      bad = __syncthreads_or(bad);
       s_part[tid] = sum;
       __syncthreads();
       // inclusive scan of the partial sums (Hillis-Steele)
@@ -1297,7 +1303,7 @@ struct GemmKernel {
       if (tid == kThreads - 1) s_start[G] = s_part[kThreads - 1];
       __syncthreads();
       gstart = s_start;
-      T = s_start[G];
+      T = bad ? 0 : s_start[G];
     }
     // Split tail: when the last round of map tiles is partial and at most half full, a second
     // launch (tail == 2, BM x BN kernel over the map of 2BM x 2BN tiles) takes it as quarter

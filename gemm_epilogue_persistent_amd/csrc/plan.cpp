@@ -51,11 +51,22 @@ static bool is_output_type(int32_t dt, bool c) {
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Largest stride (elements) and operand span (bytes) accepted: products of a stride with any
+// index stay far inside int64 on the host and in the kernels.
+constexpr int64_t kMaxStride = (int64_t)1 << 48;
+constexpr int64_t kMaxSpan = (int64_t)1 << 62;
+
 // Check one operand: contiguous extent and strides in whole 16-byte chunks, leading
-// dimension covering the contiguous extent.
+// dimension covering the contiguous extent, the whole addressed span (nb batches) bounded.
 static gemm_status check_operand(const char* name, int es, int64_t contig, int64_t ld,
-                                 int64_t other_extent, int64_t batch_stride) {
+                                 int64_t other_extent, int64_t batch_stride, int64_t nb) {
   if (ld < 0 || batch_stride < 0) return fail(GEMM_ERR_INVALID_ARG, "%s: negative stride", name);
+  if (ld > kMaxStride || batch_stride > kMaxStride)
+    return fail(GEMM_ERR_UNSUPPORTED, "%s: stride beyond 2^48 elements", name);
+  if (contig > 0 && other_extent > 0 && nb > 0) {
+    const __int128 span = ((__int128)(nb - 1) * batch_stride + (__int128)(other_extent - 1) * ld + contig) * es;
+    if (span > kMaxSpan) return fail(GEMM_ERR_UNSUPPORTED, "%s: addresses more than 2^62 bytes", name);
+  }
   if (other_extent > 1 && ld < contig)
     return fail(GEMM_ERR_INVALID_ARG, "%s: leading dimension %lld smaller than the contiguous extent %lld",
                 name, (long long)ld, (long long)contig);
@@ -155,12 +166,14 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   const int64_t rows_a = (d.gather_a && d.varlen_m) ? d.gather_rows : M;  // rows A's pointer addresses
   const int64_t cols_a = (d.gather_a && d.varlen_k) ? d.gather_rows : K;  // its K extent
   gemm_status st;
-  if (d.a_major == GEMM_ROW) st = check_operand("A", es_a, K, d.lda, rows_a, a_batched ? d.sa : 0);
-  else st = check_operand("A", es_a, M, d.lda, cols_a, a_batched ? d.sa : 0);
+  const int64_t nb_a = a_batched ? d.L : 1;
+  if (d.a_major == GEMM_ROW) st = check_operand("A", es_a, K, d.lda, rows_a, a_batched ? d.sa : 0, nb_a);
+  else st = check_operand("A", es_a, M, d.lda, cols_a, a_batched ? d.sa : 0, nb_a);
   if (st != GEMM_OK) return st;
   const bool b_batched = d.varlen_m ? d.L > 1 : (batched && !d.varlen_k);
-  if (d.b_major == GEMM_ROW) st = check_operand("B", es_b, K, d.ldb, N, b_batched ? d.sb : 0);
-  else st = check_operand("B", es_b, N, d.ldb, K, b_batched ? d.sb : 0);
+  const int64_t nb_b = b_batched ? d.L : 1;
+  if (d.b_major == GEMM_ROW) st = check_operand("B", es_b, K, d.ldb, N, b_batched ? d.sb : 0, nb_b);
+  else st = check_operand("B", es_b, N, d.ldb, K, b_batched ? d.sb : 0, nb_b);
   if (st != GEMM_OK) return st;
   struct { const char* n; int32_t dt; int64_t ld, s; } xo[3] = {
       {"C", d.c, d.ldc, d.sc}, {"D", d.d, d.ldd, d.sd}, {"PostAct", d.post, d.ldp, d.sp}};
@@ -168,10 +181,10 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
     if (xo[i].dt == DT_NONE) continue;
     int es = elem_bytes(xo[i].dt);
     int64_t contig = out_major == GEMM_ROW ? N : M, other = out_major == GEMM_ROW ? M : N;
-    st = check_operand(xo[i].n, es, contig, xo[i].ld, other, batched ? xo[i].s : 0);
+    st = check_operand(xo[i].n, es, contig, xo[i].ld, other, batched ? xo[i].s : 0, batched ? d.L : 1);
     if (st != GEMM_OK) return st;
     // written outputs of different batches must not overlap
-    if (i > 0 && batched && other > 0 && xo[i].s < other * xo[i].ld)
+    if (i > 0 && batched && other > 0 && (__int128)xo[i].s < (__int128)other * xo[i].ld)
       return fail(GEMM_ERR_INVALID_ARG, "%s: batch stride overlaps the previous batch", xo[i].n);
   }
 

@@ -196,7 +196,8 @@ typedef struct gemm_plan gemm_plan;
  * says why: INVALID_ARG (NULL desc/out, a negative size, strides smaller than the
  * extents they skip, unknown enum value), UNSUPPORTED (dtype or major combination the
  * pages exclude or this library does not build, tile pair not offered, tile count >= 2^31,
- * a tile's operand byte offsets >= 2^31), ALIGNMENT (contiguous extent or stride not a
+ * a tile's operand byte offsets >= 2^31, a stride beyond 2^48 elements, an operand whose
+ * addressed span exceeds 2^62 bytes), ALIGNMENT (contiguous extent or stride not a
  * multiple of 16 bytes), NO_MEMORY. Zero sizes are valid: M, N or L == 0 is an empty
  * problem, and K == 0 makes the product zero (page 5, GemmSm90.mma sets the accumulator
  * to zero when there is no k-tile). */
@@ -209,8 +210,9 @@ gemm_status gemm_create(const gemm_desc* desc, gemm_plan** out);
  * alpha_dev / beta_dev: optional device pointers to one fp32 each; when non-NULL they
  * replace desc.alpha / desc.beta and are read by the kernel at run time (page 5,
  * gemm_sm90 passes a tensor alpha/beta to the kernel as a pointer).
- * cu_seqlens_m: device int32[L+1], required iff varlen_m; precondition (not checked):
- * cu[0] == 0, non-decreasing, cu[L] == M. Returns INVALID_ARG for a missing pointer,
+ * cu_seqlens_m: device int32[L+1], required iff varlen_m; precondition: cu[0] == 0,
+ * non-decreasing, cu[L] == M (checked by the kernel: an array that breaks it runs no tile and
+ * writes nothing; gemm_check_cu_seqlens reports it). Returns INVALID_ARG for a missing pointer,
  * ALIGNMENT for a pointer that is not 16-byte aligned, HIP if the launch fails. */
 gemm_status gemm_run(const gemm_plan* plan, const void* A, const void* B, const void* C, void* D,
                      void* PostAct, const float* alpha_dev, const float* beta_dev,
@@ -272,6 +274,19 @@ gemm_status gemm_run_dynamic(const gemm_plan* plan, const void* A, const void* B
 gemm_status gemm_run_dynamic_noalloc(const gemm_plan* plan, const void* A, const void* B, const void* C,
                                      void* D, void* PostAct, const float* alpha_dev,
                                      const float* beta_dev, const int32_t* cu_seqlens_m, void* stream);
+
+/* Debug check of a cu_seqlens array (page 5: cu_seqlens_m / cu_seqlens_k delimit the groups
+ * of the varlen modes; their well-formedness is the caller's precondition there). Enqueues one
+ * small kernel that writes int32 *status_dev = 0 when cu[0] == 0, cu never decreases and
+ * cu[L] == total (exact_end = 1, varlen-M: total = M) or cu[L] <= total (exact_end = 0,
+ * varlen-K: total = K); otherwise 1 + the index of the first entry that breaks a rule.
+ * cu_seqlens: device int32[L+1]; status_dev: device int32, caller-owned. Asynchronous on
+ * `stream`: read the status after synchronising. The varlen-M kernels make the same check on
+ * every launch and, for an array that fails it, run no tile and write nothing. INVALID_ARG for
+ * a NULL pointer, L < 0, total < 0 or exact_end not 0/1; ALIGNMENT for pointers not 4-byte
+ * aligned; HIP if the launch fails. */
+gemm_status gemm_check_cu_seqlens(const int32_t* cu_seqlens, int32_t L, int32_t total, int32_t exact_end,
+                                  int32_t* status_dev, void* stream);
 
 /* Release a plan (NULL is accepted). */
 gemm_status gemm_destroy(gemm_plan* plan);

@@ -106,6 +106,9 @@ def test_create_accepts_valid(lib):
     (dict(N=100, ldd=256), _abi.ALIGNMENT),
     (dict(c=_abi.DT["bf16"], ldc=256, c_major=_abi.COL), _abi.UNSUPPORTED),  # mixed output majors
     (dict(tile_m=64, tile_n=64), _abi.UNSUPPORTED),
+    (dict(lda=1 << 49), _abi.UNSUPPORTED),  # stride beyond 2^48 elements
+    (dict(L=1 << 15, sa=65536, sb=65536, sd=(1 << 48) - 8), _abi.UNSUPPORTED),  # D spans 2^64 bytes
+    (dict(M=1 << 30, ldd=1 << 33, K=16, lda=16), _abi.UNSUPPORTED),  # D spans 2^64 bytes
     (dict(group_m=3), _abi.INVALID_ARG),
     (dict(group_m=32), _abi.INVALID_ARG),
     (dict(xcd_remap=2), _abi.INVALID_ARG),

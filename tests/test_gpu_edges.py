@@ -96,3 +96,44 @@ def test_f32_dact_ragged_half_group(tile):
     tol, rms = tol_for(inp)
     check_close(d, pre, tol, rms, "D")
     check_close(p, postv, tol, rms, "PostAct")
+
+
+# ---------------------------------------------------------------------------------------
+# malformed cu_seqlens: reported by gemm_check_cu_seqlens; the varlen-M kernels run no tile
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cu,total,exact,want", [
+    ([0, 300, 300, 557], 557, True, 0),
+    ([0], 0, True, 0),
+    ([1, 300, 557], 557, True, 1),        # does not start at 0
+    ([0, 300, 200, 557], 557, True, 3),   # decreases at index 2
+    ([0, 300, 556], 557, True, 3),        # ends short of M
+    ([0, 300, 600], 557, True, 3),        # ends past M
+    ([0, 64, 64, 128], 200, False, 0),    # varlen-K: may end before K
+    ([0, 64, 300], 200, False, 3),        # ... but not past it
+])
+def test_check_cu_seqlens(cu, total, exact, want):
+    from gemm_epilogue_persistent_amd import check_cu_seqlens
+    st = check_cu_seqlens(torch.tensor(cu, dtype=torch.int32, device="cuda"), total, exact)
+    torch.cuda.synchronize()
+    assert int(st.item()) == want
+
+
+@pytest.mark.parametrize("cu_bad", [[0, 300, 200, 520], [0, 256, 520 + 256], [8, 264, 520], [0, 100, 500]])
+def test_varlen_bad_cu_seqlens_writes_nothing(cu_bad):
+    """M = 520 rows in the plan; each array breaks a rule (decreasing, past M, not from 0, short
+    of M). The output buffer holds 512 rows more than M, so that even rows addressed past M
+    stay inside it: all of it must still hold the sentinel afterwards."""
+    from gemm_epilogue_persistent_amd import Plan
+    M, N, K = 520, 264, 64
+    G = len(cu_bad) - 1
+    A = W.normal(2200, (M, K), "bf16", 0.5).cuda()
+    B = W.normal(2201, (G, N, K), "bf16", 0.5).cuda()
+    buf = torch.full((M + 512, N), SENTINEL, dtype=torch.float32, device="cuda")
+    D = buf[:M]
+    cu = torch.tensor(cu_bad, dtype=torch.int32, device="cuda")
+    announce(f"varlen bad cu_seqlens {cu_bad}")
+    plan = Plan(A, B, None, D, None, cu_seqlens_m=cu)
+    plan.run(A, B, None, D, None, cu_seqlens_m=cu)
+    torch.cuda.synchronize()
+    assert (buf == SENTINEL).all()
