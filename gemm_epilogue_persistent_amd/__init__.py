@@ -27,7 +27,7 @@ _TORCH_DT = {torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32",
              torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}
 
 __all__ = ["Plan", "gemm", "gemm_dact", "gemm_create", "gemm_run", "plan_grid", "configs", "tune", "fastdivmod_params",
-           "fastdivmod_check", "check_cu_seqlens", "GemmError", "library_path"]
+           "fastdivmod_check", "check_cu_seqlens", "tuned_config", "GemmError", "library_path"]
 
 
 def library_path():
@@ -226,8 +226,12 @@ class Plan:
 
 
 def gemm(A, B, D=None, C=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu_seqlens_m=None,
-         alpha_dev=None, beta_dev=None, stream=None, cu_seqlens_k=None, a_idx=None, **tuning):
-    """One-shot call: plan (validated on the host) and enqueue. Outputs are written in place."""
+         alpha_dev=None, beta_dev=None, stream=None, cu_seqlens_k=None, a_idx=None, autotune=False, **tuning):
+    """One-shot call: plan (validated on the host) and enqueue. Outputs are written in place.
+    autotune=True (dense and varlen-M plans): the configuration tune() found fastest for this
+    problem signature, timed once per process and cached (see tuned_config)."""
+    if autotune and not tuning and cu_seqlens_k is None and a_idx is None:
+        tuning = tuned_config(A, B, C, D, PostAct, alpha, beta, act, cu_seqlens_m)
     p = Plan(A, B, C, D, PostAct, alpha, beta, act, cu_seqlens_m, cu_seqlens_k, a_idx, **tuning)
     p.run(A, B, C, D, PostAct, alpha_dev, beta_dev, cu_seqlens_m, stream, cu_seqlens_k=cu_seqlens_k,
           a_idx=a_idx)
@@ -283,6 +287,30 @@ def tune(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu
         timed.append((start.elapsed_time(end) / steps, tun))
     timed.sort(key=lambda x: x[0])
     return timed[0][1], timed
+
+
+_TUNED = {}
+
+
+def _signature(A, B, C, D, PostAct, act, cu_seqlens_m):
+    """What a configuration's speed depends on: shapes, strides, types, epilogue kind and, for
+    varlen-M, the group sizes (the tile count and balance follow from them)."""
+    sig = [act, None if cu_seqlens_m is None else tuple(cu_seqlens_m.tolist())]
+    for t in (A, B, C, D, PostAct):
+        sig.append(None if t is None else (tuple(t.shape), tuple(t.stride()), str(t.dtype)))
+    return tuple(sig)
+
+
+def tuned_config(A, B, C=None, D=None, PostAct=None, alpha=1.0, beta=1.0, act="none", cu_seqlens_m=None,
+                 candidates=None, steps=10, warmup=3):
+    """The fastest configuration for this problem signature: timed with tune() on the first call
+    (the outputs are overwritten then), looked up afterwards. Every configuration computes the
+    same bits, so the choice changes only the speed."""
+    key = _signature(A, B, C, D, PostAct, act, cu_seqlens_m)
+    if key not in _TUNED:
+        best, _ = tune(A, B, C, D, PostAct, alpha, beta, act, cu_seqlens_m, candidates, steps, warmup)
+        _TUNED[key] = best
+    return dict(_TUNED[key])
 
 
 def fastdivmod_params(d):

@@ -1030,12 +1030,25 @@ struct GemmKernel {
     }
   }
 
-  // Four outputs of the generic pass (any C / D / PostAct types), at 4-element pointers.
+  // Four outputs of the generic pass (any C / D / PostAct types), at 4-element pointers. With
+  // a transposed C (c_trans) its four values lie cstride bytes apart.
   static __device__ __forceinline__ void finish4(const KParams& p, const char* cp, char* dp, char* pp,
-                                                 const f32x4& x, float alpha, float beta) {
+                                                 const f32x4& x, float alpha, float beta, int64_t cstride) {
     float v[4] = {x[0] * alpha, x[1] * alpha, x[2] * alpha, x[3] * alpha};
     float c[4] = {0.f, 0.f, 0.f, 0.f};
-    if (p.c_dt != DT_NONE) {
+    if (p.c_dt != DT_NONE && p.c_trans) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const char* q = cp + e * cstride;
+        if (p.c_dt == DT_F32) c[e] = *(const float*)q;
+        else if (p.c_dt == DT_BF16) c[e] = __uint_as_float((uint32_t)*(const uint16_t*)q << 16);
+        else c[e] = (float)*(const _Float16*)q;
+      }
+      if constexpr (!DACT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c[e], v[e]);
+      }
+    } else if (p.c_dt != DT_NONE) {
       if (p.c_dt == DT_F32) {
         const f32x4 y = *(const f32x4*)cp;
         c[0] = y[0]; c[1] = y[1]; c[2] = y[2]; c[3] = y[3];
@@ -1085,8 +1098,9 @@ struct GemmKernel {
         const int n = 8 * c8 + 4 * hf;
         if (n + 4 > ea.cols_valid) continue;
         const f32x4 x = *(const f32x4 GEP_LDS*)(buf + ebuf(r, c8, hf));
-        finish4(p, ea.cb + ((int64_t)m * p.ldc + n) * esc, ea.db + ((int64_t)m * p.ldd + n) * esd,
-                ea.pb + ((int64_t)m * p.ldp + n) * esp, x, ea.alpha, ea.beta);
+        const int64_t coff = p.c_trans ? (int64_t)n * p.ldc + m : (int64_t)m * p.ldc + n;
+        finish4(p, ea.cb + coff * esc, ea.db + ((int64_t)m * p.ldd + n) * esd,
+                ea.pb + ((int64_t)m * p.ldp + n) * esp, x, ea.alpha, ea.beta, p.ldc * esc);
       }
     }
   }
@@ -1154,7 +1168,8 @@ struct GemmKernel {
     const int row0 = ti.m0 + wm0, col0 = ti.n0 + wn0;
     const int esc = dt_bytes(p.c_dt), esd = dt_bytes(p.d_dt), esp = dt_bytes(p.p_dt);
     EpiArgs ea;
-    ea.cb = (const char*)p.C + ((VARLEN ? 0 : (int64_t)ti.l * p.sc) + (int64_t)row0 * p.ldc + col0) * esc;
+    ea.cb = (const char*)p.C + ((VARLEN ? 0 : (int64_t)ti.l * p.sc) +
+                                (p.c_trans ? (int64_t)col0 * p.ldc + row0 : (int64_t)row0 * p.ldc + col0)) * esc;
     ea.db = (char*)p.D + ((VARLEN ? 0 : (int64_t)ti.l * p.sd) + (int64_t)row0 * p.ldd + col0) * esd;
     ea.pb = (char*)p.Post + ((VARLEN ? 0 : (int64_t)ti.l * p.sp) + (int64_t)row0 * p.ldp + col0) * esp;
     ea.rows_valid = ti.row_end - row0;
@@ -1182,7 +1197,7 @@ struct GemmKernel {
     }
     // one output type for C, D and PostAct (those present), 16-bit: the branch-free path
     const int ot = p.d_dt != DT_NONE ? p.d_dt : p.p_dt;
-    const bool same = (p.c_dt == DT_NONE || p.c_dt == ot) && (p.p_dt == DT_NONE || p.p_dt == ot);
+    const bool same = (p.c_dt == DT_NONE || (p.c_dt == ot && !p.c_trans)) && (p.p_dt == DT_NONE || p.p_dt == ot);
     const int path = !same ? 0 : (ot == DT_BF16 ? 1 : (ot == DT_F16 ? 2 : 0));
 #pragma unroll 1
     for (int pass = 0; pass < kMI / kBPP; ++pass) {

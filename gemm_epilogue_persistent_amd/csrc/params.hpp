@@ -32,6 +32,7 @@ struct KParams {
   const int32_t* a_idx;       // gathered A rows (varlen-M), or NULL
   int32_t a_rows;             // rows of A that a_idx may name
   int32_t c_dt, d_dt, p_dt;
+  int32_t c_trans;  // C's contiguous dimension is the kernel's M (the outputs' is N)
   int32_t act;
   // persistent schedule
   int32_t tm, tn;   // M- and N-blocks (tm unused for varlen)

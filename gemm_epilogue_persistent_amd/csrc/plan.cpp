@@ -130,15 +130,17 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
     return fail(GEMM_ERR_INVALID_ARG, "an activation needs a PostAct output");
   }
 
-  // ---- output majors
+  // ---- output majors: D and PostAct share one; C may have either (page 5, gemm_sm90 reads
+  // each operand's major mode from its own strides)
   int32_t out_major = -1;
   const int32_t omaj[3] = {d.c_major, d.d_major, d.post_major};
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 1; i < 3; ++i) {
     if (outs[i] == DT_NONE) continue;
     if (out_major == -1) out_major = omaj[i];
-    else if (out_major != omaj[i]) return fail(GEMM_ERR_UNSUPPORTED, "C, D and PostAct must share one major mode");
+    else if (out_major != omaj[i]) return fail(GEMM_ERR_UNSUPPORTED, "D and PostAct must share one major mode");
   }
-  if (d.varlen_m && out_major == GEMM_COL)
+  const bool c_trans = d.c != DT_NONE && d.c_major != out_major;
+  if (d.varlen_m && (out_major == GEMM_COL || c_trans))
     return fail(GEMM_ERR_UNSUPPORTED, "varlen-M needs N-major C/D/PostAct");
   if (d.gather_a && d.varlen_m && (es_a != 2 || d.a_major != GEMM_ROW))
     return fail(GEMM_ERR_UNSUPPORTED, "gathered A rows (varlen-M): A must be a 16-bit K-major operand");
@@ -180,7 +182,8 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   for (int i = 0; i < 3; ++i) {
     if (xo[i].dt == DT_NONE) continue;
     int es = elem_bytes(xo[i].dt);
-    int64_t contig = out_major == GEMM_ROW ? N : M, other = out_major == GEMM_ROW ? M : N;
+    const int32_t maj = i == 0 ? d.c_major : out_major;
+    int64_t contig = maj == GEMM_ROW ? N : M, other = maj == GEMM_ROW ? M : N;
     st = check_operand(xo[i].n, es, contig, xo[i].ld, other, batched ? xo[i].s : 0, batched ? d.L : 1);
     if (st != GEMM_OK) return st;
     // written outputs of different batches must not overlap
@@ -239,6 +242,7 @@ gemm_status create_plan(const gemm_desc* d_in, gemm_plan** out) {
   k.alpha = d.alpha;
   k.beta = d.beta;
   k.c_dt = d.c;
+  k.c_trans = c_trans ? 1 : 0;
   k.d_dt = d.d;
   k.p_dt = d.post;
   k.act = d.act;

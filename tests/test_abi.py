@@ -73,6 +73,10 @@ def test_create_accepts_valid(lib):
     assert create(lib, d) == _abi.OK
     d = base_desc(c=_abi.DT["f32"], ldc=256, post=_abi.DT["bf16"], ldp=256, act=_abi.ACT["gelu_tanh"])
     assert create(lib, d) == _abi.OK
+    # C in the other major mode than D (either way round), dact included
+    assert create(lib, base_desc(c=_abi.DT["bf16"], ldc=256, c_major=_abi.COL)) == _abi.OK
+    assert create(lib, base_desc(c=_abi.DT["f32"], ldc=256, d_major=_abi.COL)) == _abi.OK
+    assert create(lib, base_desc(c=_abi.DT["f16"], ldc=256, c_major=_abi.COL, dact=1)) == _abi.OK
     # varlen-K: A (M, K) M-major, B (N, K) N-major, D (L, M, N); M-major D as well
     d = base_desc(varlen_k=1, L=4, a_major=_abi.COL, b_major=_abi.COL, sd=65536)
     assert create(lib, d) == _abi.OK
@@ -104,7 +108,8 @@ def test_create_accepts_valid(lib):
     (dict(lda=260), _abi.ALIGNMENT),
     (dict(lda=128), _abi.INVALID_ARG),  # leading dimension below K
     (dict(N=100, ldd=256), _abi.ALIGNMENT),
-    (dict(c=_abi.DT["bf16"], ldc=256, c_major=_abi.COL), _abi.UNSUPPORTED),  # mixed output majors
+    (dict(post=_abi.DT["bf16"], ldp=256, post_major=_abi.COL), _abi.UNSUPPORTED),  # D and PostAct majors differ
+    (dict(varlen_m=1, L=2, sb=65536, c=_abi.DT["bf16"], ldc=256, c_major=_abi.COL), _abi.UNSUPPORTED),
     (dict(tile_m=64, tile_n=64), _abi.UNSUPPORTED),
     (dict(lda=1 << 49), _abi.UNSUPPORTED),  # stride beyond 2^48 elements
     (dict(L=1 << 15, sa=65536, sb=65536, sd=(1 << 48) - 8), _abi.UNSUPPORTED),  # D spans 2^64 bytes

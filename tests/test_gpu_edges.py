@@ -137,3 +137,44 @@ def test_varlen_bad_cu_seqlens_writes_nothing(cu_bad):
     plan.run(A, B, None, D, None, cu_seqlens_m=cu)
     torch.cuda.synchronize()
     assert (buf == SENTINEL).all()
+
+
+# ---------------------------------------------------------------------------------------
+# C in the other major mode than D / PostAct (each operand's major from its own strides)
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+@pytest.mark.parametrize("d_mmaj", [False, True])
+@pytest.mark.parametrize("c_dt,out_dt", [("bf16", "bf16"), ("f32", "f16"), ("f16", "f32")])
+def test_c_transposed(tile, d_mmaj, c_dt, out_dt):
+    from parity import run_hip
+    M, N, K, L = 264, 392, 136, 2
+    A = W.normal(2300, (L, M, K), "bf16", 0.5)
+    B = W.normal(2301, (L, N, K), "bf16", 0.5)
+    # C's contiguous dimension is the other one than the outputs'
+    C = W.normal(2302, (L, M, N), c_dt) if d_mmaj else W.normal(2302, (L, N, M), c_dt).permute(0, 2, 1)
+    inp = W.Inputs("c_trans", M, N, K, L, "bf16", "bf16", A, B, C=C, c_dt=c_dt, d_dt=out_dt,
+                   post_dt=out_dt, alpha=0.75, beta=-1.5, act="gelu_tanh")
+    announce(f"C transposed tile={tile} d_mmaj={d_mmaj} C={c_dt} out={out_dt}")
+    d, p, _ = run_hip(inp, d_major_m=d_mmaj, tile=tile)
+    pre, post = problem_of(inp).all(*oracle_codes(inp))
+    tol, rms = tol_for(inp)
+    check_close(d, pre, tol, rms, "D")
+    check_close(p, post, tol, rms, "PostAct")
+
+
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_c_transposed_dact(tile):
+    from parity import run_hip
+    M, N, K = 200, 264, 72
+    A = W.normal(2310, (1, M, K), "bf16", 0.5)
+    B = W.normal(2311, (1, N, K), "bf16", 0.5)
+    C = W.normal(2312, (1, N, M), "bf16", 1.5).permute(0, 2, 1)  # M-contiguous pre-activation
+    inp = W.Inputs("c_trans_dact", M, N, K, 1, "bf16", "bf16", A, B, C=C, c_dt="bf16", d_dt="bf16",
+                   post_dt="bf16", act="silu", dact=True)
+    announce(f"C transposed dact tile={tile}")
+    d, p, _ = run_hip(inp, tile=tile)
+    pre, post = problem_of(inp).all(*oracle_codes(inp))
+    tol, rms = tol_for(inp)
+    check_close(d, pre, tol, rms, "D")
+    check_close(p, post, tol, rms, "PostAct")

@@ -391,6 +391,22 @@ def test_raster_along_n_results():
     assert np.array_equal(d_n, d_m) and np.array_equal(p_n, p_m)
 
 
+def test_autotune_caches_the_tuned_choice():
+    from gemm_epilogue_persistent_amd import configs, gemm, tuned_config
+    inp = small(1100, 1200, 64, 1, "bf16", d_dt="bf16", seed=46)
+    d_ref, _, _ = run_hip(inp)
+    A, B = to_dev(inp.A), to_dev(inp.B)
+    D = out_like(inp, "bf16")
+    cands = configs()[::7]
+    first = tuned_config(A, B, D=D, candidates=cands, steps=2, warmup=1)
+    assert first in cands
+    assert tuned_config(A, B, D=D, candidates=[]) == first  # cached: not timed again
+    D.fill_(float("nan"))
+    gemm(A, B, D, autotune=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(D.double().cpu().numpy(), d_ref)
+
+
 def test_tune_picks_a_config_with_identical_results():
     from gemm_epilogue_persistent_amd import configs, tune
     inp = small(1100, 1200, 64, 1, "f16", d_dt="f16", seed=45)
