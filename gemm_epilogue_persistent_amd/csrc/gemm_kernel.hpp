@@ -505,7 +505,7 @@ struct GemmKernel {
   static constexpr int kBOff = 2 * kStageBytes;
   static constexpr int kLdsBytes = 4 * kStageBytes;
   // varlen group table (tile offsets of the groups, scan partials) past the ring
-  static constexpr int kVarlenLds = (kMaxVarlenGroups + 1 + kThreads) * 4;
+  static constexpr int kVarlenLds = (kMaxVarlenGroups + 1 + kThreads + 1) * 4;  // (+1: the validity flag)
   static constexpr int kSlotBytes = 16;  // dynamic schedule: next queue position
   static constexpr int kFrags = kMI + kNI;
   static constexpr int kMfmaPerStep = kMI * kNI;
@@ -1279,6 +1279,12 @@ struct GemmKernel {
     if constexpr (VARLEN) {
       int32_t* s_start = (int32_t*)(smem_raw + kLdsBytes + kSlotBytes);
       int32_t* s_part = s_start + kMaxVarlenGroups + 1;
+      // the validity flag lives in the same LDS array (__syncthreads_or would add an LDS object
+      // of its own, and with two the compiler waits for every pending global -> LDS transfer
+      // before each fragment read)
+      volatile int32_t* s_bad = s_part + kThreads;
+      if (tid == 0) *s_bad = 0;
+      __syncthreads();
       const int G = p.L;
       constexpr int kPer = (kMaxVarlenGroups + kThreads - 1) / kThreads;
       int32_t local[kPer];
@@ -1299,9 +1305,10 @@ struct GemmKernel {
         local[q] = sum;
         sum += tiles;
       }
-      bad = __syncthreads_or(bad);
+      if (bad) *s_bad = 1;
       s_part[tid] = sum;
       __syncthreads();
+      bad = __builtin_amdgcn_readfirstlane(*s_bad);
       // inclusive scan of the partial sums (Hillis-Steele)
       for (int off = 1; off < kThreads; off <<= 1) {
         const int32_t add = tid >= off ? s_part[tid - off] : 0;
@@ -1318,7 +1325,7 @@ struct GemmKernel {
       if (tid == kThreads - 1) s_start[G] = s_part[kThreads - 1];
       __syncthreads();
       gstart = s_start;
-      T = bad ? 0 : s_start[G];
+      T = __builtin_amdgcn_readfirstlane(bad ? 0 : s_start[G]);
     }
     // Split tail: when the last round of map tiles is partial and at most half full, a second
     // launch (tail == 2, BM x BN kernel over the map of 2BM x 2BN tiles) takes it as quarter
