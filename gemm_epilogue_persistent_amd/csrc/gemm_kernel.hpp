@@ -53,45 +53,82 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------------------------
-// MFMA flavours. Frag = the per-lane operand registers of one 32-row fragment.
-// Lane l holds row (l % 32) and, inside the instruction's K slice, elements [8*(l/32), +8)
-// for 16-bit types or bytes [32*(l/32), +32) for fp8; A and B use the same K assignment.
-// The kernel passes the B fragment as the instruction's first source and the A fragment as
-// its second, so that each output lane holds 4 consecutive N values (see the epilogue).
+// MFMA flavours, in blocks of kBlk x kBlk outputs. Frag = the per-lane operand registers of
+// one kBlk-row fragment: lane l holds row (l % kBlk) and, inside the instruction's K slice,
+// the (l / kBlk)-th run of 8 16-bit elements or 32 fp8 bytes; A and B use the same K
+// assignment. The kernel passes the B fragment as the instruction's first source and the A
+// fragment as its second, so that each output lane holds 4 consecutive N values (see the
+// epilogue).
+// Measured on gfx950 with full-entropy operands and no memory traffic, the chip sustains the
+// 16x16 forms at a higher clock than the 32x32 ones (the same FLOPs take less energy):
+// bf16 16x16x32 2.06 against 32x32x16 1.84 PFLOP/s with two waves per SIMD; fp8 16x16x128
+// 4.41 against 32x32x64 4.07 PFLOP/s with one.
 // ------------------------------------------------------------------------------------
-template <int OP, int FA, int FB>
+template <int OP, int FA, int FB, int BLK = 32>
 struct Mfma;
 
 template <int FA, int FB>
-struct Mfma<OP_F16, FA, FB> {
+struct Mfma<OP_F16, FA, FB, 32> {
   static constexpr int kES = 2;       // bytes per element
   static constexpr int kKStep = 16;   // K per instruction
+  static constexpr int kBlk = 32;
   using Frag = i32x4;
-  static __device__ __forceinline__ f32x16 mma(Frag b, Frag a, f32x16 c) {
+  using Acc = f32x16;
+  static __device__ __forceinline__ Acc mma(Frag b, Frag a, Acc c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, b), __builtin_bit_cast(f16x8, a),
                                                   c, 0, 0, 0);
   }
 };
 
 template <int FA, int FB>
-struct Mfma<OP_BF16, FA, FB> {
+struct Mfma<OP_BF16, FA, FB, 32> {
   static constexpr int kES = 2;
   static constexpr int kKStep = 16;
+  static constexpr int kBlk = 32;
   using Frag = i32x4;
-  static __device__ __forceinline__ f32x16 mma(Frag b, Frag a, f32x16 c) {
+  using Acc = f32x16;
+  static __device__ __forceinline__ Acc mma(Frag b, Frag a, Acc c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a),
                                                    c, 0, 0, 0);
   }
 };
 
 template <int FA, int FB>
-struct Mfma<OP_FP8, FA, FB> {
+struct Mfma<OP_F16, FA, FB, 16> {
+  static constexpr int kES = 2;
+  static constexpr int kKStep = 32;
+  static constexpr int kBlk = 16;
+  using Frag = i32x4;
+  using Acc = f32x4;
+  static __device__ __forceinline__ Acc mma(Frag b, Frag a, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, b), __builtin_bit_cast(f16x8, a),
+                                                  c, 0, 0, 0);
+  }
+};
+
+template <int FA, int FB>
+struct Mfma<OP_BF16, FA, FB, 16> {
+  static constexpr int kES = 2;
+  static constexpr int kKStep = 32;
+  static constexpr int kBlk = 16;
+  using Frag = i32x4;
+  using Acc = f32x4;
+  static __device__ __forceinline__ Acc mma(Frag b, Frag a, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a),
+                                                   c, 0, 0, 0);
+  }
+};
+
+template <int FA, int FB>
+struct Mfma<OP_FP8, FA, FB, 32> {
   static constexpr int kES = 1;
   static constexpr int kKStep = 64;
+  static constexpr int kBlk = 32;
   using Frag = i32x8;
+  using Acc = f32x16;
   // cbsz / blgp select the format of the first / second source (0 = e4m3, 1 = e5m2):
   // B's format goes in cbsz and A's in blgp. Scales of 127 are 2^0 in E8M0 (no scaling).
-  static __device__ __forceinline__ f32x16 mma(Frag b, Frag a, f32x16 c) {
+  static __device__ __forceinline__ Acc mma(Frag b, Frag a, Acc c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, 0, 127, 0, 127);
   }
 };
@@ -261,25 +298,31 @@ struct TileLoader {
 template <bool KMAJ, int ES>
 constexpr int reads_per_frag() { return KMAJ ? (ES == 2 ? 1 : 2) : 2; }
 
-// Fragment reader: rows [r0, r0+32) of a tile, MFMA k-step s of the k-tile.
+// Fragment reader: rows [r0, r0 + kBlk) of a tile, MFMA k-step s of the k-tile.
+// (16x16 reads: the 16 lanes of a ds_read_b128 phase hold rows {0-3, 8-11} of one chunk and
+// rows {4-7, 12-15} of the next, which the K-major key also spreads over 16 distinct slots.)
 template <bool KMAJ, int ROWS, class Op, bool PAD>
 __device__ __forceinline__ typename Op::Frag read_frag(const GEP_LDS char* tile, int r0, int s, int lane) {
   using Frag = typename Op::Frag;
+  constexpr int kB = Op::kBlk;
   if constexpr (KMAJ) {
-    const int row = r0 + (lane & 31);
+    const int row = r0 + (lane & (kB - 1));
+    const int kg = lane / kB;  // the lane's run of K inside the instruction's K slice
     const int sw = PAD ? 0 : kswz(row);
     const GEP_LDS char* rp = tile + row * (PAD ? kRowBytes + 16 : kRowBytes);
     if constexpr (Op::kES == 2) {
-      const int c = s * 2 + (lane >> 5);
+      const int c = s * (64 / kB) + kg;
       return *(const GEP_LDS i32x4*)(rp + ((c ^ sw) << 4));
     } else {
-      const int c = s * 4 + (lane >> 5) * 2;  // 32 bytes per lane: two chunks
+      static_assert(kB == 32, "fp8 fragments are read for the 32x32 form");
+      const int c = s * 4 + kg * 2;  // 32 bytes per lane: two chunks
       i32x4 lo = *(const GEP_LDS i32x4*)(rp + ((c ^ sw) << 4));
       i32x4 hi = *(const GEP_LDS i32x4*)(rp + (((c + 1) ^ sw) << 4));
       return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   } else {
     static_assert(Op::kES == 2, "M/N-major operands are 16-bit only");
+    static_assert(kB == 32, "M/N-major fragments are read for the 32x32 form");
     // Source lane (in its 16-lane group) 4j + a reads the 4 row-contiguous elements at
     // k-row kb + j, rows r0 + 16*(group & 1) + 4a; after the transpose lane 4a + e holds
     // row 4a + e, k-rows kb + 0..3.
@@ -468,7 +511,7 @@ struct TileInfo {
 // VM: 0 dense batched, 1 varlen-M (cu_seqlens splits the rows), 2 varlen-K (cu_seqlens
 // splits K; one output batch per group). GA: A rows gathered through a_idx (varlen-M).
 template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, int VM, int NW, bool DACT = false,
-          bool GA = false>
+          bool GA = false, int BLK = 0>
 struct GemmKernel {
   static constexpr bool VARLEN = VM == 1;
   static constexpr bool VARK = VM == 2;
@@ -476,13 +519,17 @@ struct GemmKernel {
   static constexpr bool GAK = GA && VARK;  // gathered k-rows of A
   // NW wave64s in a 2 x (NW/2) grid over the output tile
   static constexpr int kThreads = NW * 64;
-  using Op = Mfma<OP, FA, FB>;
+  // MFMA block: 16x16 for the 8-wave kernels (two waves per SIMD, K-major 16-bit operands),
+  // 32x32 otherwise (BLK overrides)
+  static constexpr int kBlk = BLK ? BLK : (NW == 8 ? 16 : 32);
+  using Op = Mfma<OP, FA, FB, kBlk>;
   using Frag = typename Op::Frag;
+  using Acc = typename Op::Acc;
   static constexpr int kES = Op::kES;
   static constexpr int kBK = kRowBytes / kES;             // K elements per k-tile
   static constexpr int kSteps = kBK / Op::kKStep;          // MFMA k-steps per k-tile (4 or 2)
   static constexpr int kWM = BM / 2, kWN = BN / (NW / 2);  // per-wave output block
-  static constexpr int kMI = kWM / 32, kNI = kWN / 32;     // 32x32 MFMA blocks per wave
+  static constexpr int kMI = kWM / kBlk, kNI = kWN / kBlk;  // MFMA blocks per wave
   // kDMA: k-tiles go global -> LDS directly (buffer_load ... lds), all chunks of k-tile
   // kt+2 issued in the last MFMA step of k-tile kt; else through the staging registers
   // over the first kWriteSteps steps. Measured: direct transfers win for fp8 (they free the
@@ -517,8 +564,10 @@ struct GemmKernel {
   // 16-bit global -> LDS transfers of a k-tile are issued in two halves: the first after the
   // barrier that frees its stage, the second in the first step of the next k-tile (see ktile).
   // fp8 keeps one: its last step holds twice the MFMA work and covers the transfers (split,
-  // fp8 8192^3 measured 8% slower).
-  static constexpr int kDmaParts = (kDMA && kES == 2) ? 2 : 1;
+  // fp8 8192^3 measured 8% slower). So do 16x16 blocks, whose k-tile has two steps: the
+  // second half would land in the step that ends at the barrier waiting for it (8192^3 bf16:
+  // the younger waves' barrier time per tile 77 K -> 30 K cycles with one part).
+  static constexpr int kDmaParts = (kDMA && kES == 2 && kBlk == 32) ? 2 : 1;
   static constexpr int kChunksPerStep = kChunksPerKt / kWriteSteps / kDmaParts;
   // fragment slot f carries MFMAs [mlo(f), mlo(f+1)) and register chunks [clo(f), clo(f+1))
   static constexpr int mlo(int f) { return f * kMfmaPerStep / kFrags; }
@@ -546,7 +595,7 @@ struct GemmKernel {
     }
   }
 
-  static __device__ __forceinline__ void mma_step(f32x16 (&acc)[kMI][kNI], const Frag (&fa)[kMI],
+  static __device__ __forceinline__ void mma_step(Acc (&acc)[kMI][kNI], const Frag (&fa)[kMI],
                                                   const Frag (&fb)[kNI]) {
 #pragma unroll
     for (int i = 0; i < kMI; ++i)
@@ -557,9 +606,9 @@ struct GemmKernel {
   static __device__ __forceinline__ void read_all(Frag (&fa)[kMI], Frag (&fb)[kNI], const GEP_LDS char* st, int s,
                                                   int wm0, int wn0, int lane) {
 #pragma unroll
-    for (int i = 0; i < kMI; ++i) fa[i] = read_frag<A_K, BM, Op, kPadRows>(st, wm0 + i * 32, s, lane);
+    for (int i = 0; i < kMI; ++i) fa[i] = read_frag<A_K, BM, Op, kPadRows>(st, wm0 + i * kBlk, s, lane);
 #pragma unroll
-    for (int j = 0; j < kNI; ++j) fb[j] = read_frag<B_K, BN, Op, kPadRows>(st + kBOff, wn0 + j * 32, s, lane);
+    for (int j = 0; j < kNI; ++j) fb[j] = read_frag<B_K, BN, Op, kPadRows>(st + kBOff, wn0 + j * kBlk, s, lane);
   }
 
   // Work item u of this launch -> output tile. Tiles are numbered in the map's tiling (MT x
@@ -747,8 +796,8 @@ struct GemmKernel {
                                                int wm0, int wn0, LA& la, LB& lb, GEP_LDS char* wr,
                                                const KtSrc& src, int wave, int lane) {
     if constexpr (F < kFrags) {
-      if constexpr (F < kMI) fa[F] = read_frag<A_K, BM, Op, kPadRows>(rd, wm0 + F * 32, s, lane);
-      else fb[F - kMI] = read_frag<B_K, BN, Op, kPadRows>(rd + kBOff, wn0 + (F - kMI) * 32, s, lane);
+      if constexpr (F < kMI) fa[F] = read_frag<A_K, BM, Op, kPadRows>(rd, wm0 + F * kBlk, s, lane);
+      else fb[F - kMI] = read_frag<B_K, BN, Op, kPadRows>(rd + kBOff, wn0 + (F - kMI) * kBlk, s, lane);
       if constexpr (WR) {
         if constexpr (kDMA) dma_chunks<C0 + clo(F), clo(F + 1) - clo(F)>(la, lb, wr, src, wave);
         else cycle_chunks<C0 + clo(F), clo(F + 1) - clo(F)>(la, lb, wr, src, wave, lane);
@@ -762,7 +811,7 @@ struct GemmKernel {
   // registers (their last reader has issued), B fragment i of the next k-step (i < kNI) into
   // the other B buffer, then cycles its register chunks. Saves kMI fragment registers, which
   // lets two waves share a SIMD.
-  static constexpr bool kRoll = NW == 8;
+  static constexpr bool kRoll = NW == 8 && kBlk == 32;
   static constexpr int rlo(int i) { return i * kChunksPerStep / kMI; }
   template <bool WR, int I = 0>
   static __device__ __forceinline__ void sched_roll() {
@@ -778,14 +827,14 @@ struct GemmKernel {
     }
   }
   template <int CUR, bool WR, int C0, int I = 0>
-  static __device__ __forceinline__ void roll_slots(f32x16 (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[2][kNI],
+  static __device__ __forceinline__ void roll_slots(Acc (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[2][kNI],
                                                     const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
                                                     const KtSrc& src, int wave, int lane, int wm0, int wn0) {
     if constexpr (I < kMI) {
 #pragma unroll
       for (int j = 0; j < kNI; ++j) acc[I][j] = Op::mma(fb[CUR][j], fa[I], acc[I][j]);
-      fa[I] = read_frag<A_K, BM, Op, kPadRows>(rd, wm0 + I * 32, s, lane);
-      if constexpr (I < kNI) fb[CUR ^ 1][I] = read_frag<B_K, BN, Op, kPadRows>(rd + kBOff, wn0 + I * 32, s, lane);
+      fa[I] = read_frag<A_K, BM, Op, kPadRows>(rd, wm0 + I * kBlk, s, lane);
+      if constexpr (I < kNI) fb[CUR ^ 1][I] = read_frag<B_K, BN, Op, kPadRows>(rd + kBOff, wn0 + I * kBlk, s, lane);
       if constexpr (WR) {
         if constexpr (kDMA) dma_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave);
         else cycle_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave, lane);
@@ -794,14 +843,92 @@ struct GemmKernel {
     }
   }
 
+  // ---- column halves (kRoll3; 16x16 blocks, kMI = 2 kNI): one A and one B buffer, 12
+  // fragments live (double-buffered B with rolling A, the 32x32 scheme, needs 16 and spills
+  // next to two waves' accumulators). Slots 0 .. kNI-1 run column I over the first kH block
+  // rows, and after the last of them the A fragments of those rows are re-read; slots kNI + J
+  // run column J over the other kH rows and re-read B fragment J; the A fragments of those
+  // rows are re-read at the end. Every fragment of the next k-step is read at least kNI * kH
+  // MFMAs before its first use. (Rows first, then columns, left the last B fragment read
+  // three MFMAs before its use.)
+  static constexpr bool kRoll3 = NW == 8 && kBlk == 16;
+  static constexpr int kH = kMI / 2;
+  template <bool WR, int I, int E>
+  static __device__ __forceinline__ void sched_roll3() {
+    if constexpr (I < E) {
+      constexpr int nc = rlo(I + 1) - rlo(I);
+      constexpr int nr = I < kNI ? (I == kNI - 1 ? kH * kRA : 0) : (kRB + (I == kMI - 1 ? kH * kRA : 0));
+      __builtin_amdgcn_sched_group_barrier(0x008, kH, 0);                         // MFMAs
+      if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // LDS reads
+      if constexpr (WR && nc > 0) __builtin_amdgcn_sched_group_barrier(0x020, nc, 0);  // transfers
+      sched_roll3<WR, I + 1, E>();
+    }
+  }
+  // slots [I, E) of a step; oa / ob: this lane's fragment offsets of the k-step read, A and B
+  template <bool WR, int C0, int I, int E>
+  static __device__ __forceinline__ void roll3_slots(Acc (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[kNI],
+                                                     const GEP_LDS char* rd, int oa, int ob, LA& la, LB& lb,
+                                                     GEP_LDS char* wr, const KtSrc& src, int wave) {
+    static_assert(kMI == 2 * kNI && kDMA, "two halves of kNI block rows, global -> LDS transfers");
+    if constexpr (I < E) {
+      if constexpr (I < kNI) {
+#pragma unroll
+        for (int i = 0; i < kH; ++i) acc[i][I] = Op::mma(fb[I], fa[i], acc[i][I]);
+        if constexpr (I == kNI - 1) {
+#pragma unroll
+          for (int i = 0; i < kH; ++i) fa[i] = *(const GEP_LDS Frag*)(rd + oa + i * kBlk * kRowBytes);
+        }
+      } else {
+        constexpr int J = I - kNI;
+#pragma unroll
+        for (int i = kH; i < kMI; ++i) acc[i][J] = Op::mma(fb[J], fa[i], acc[i][J]);
+        fb[J] = *(const GEP_LDS Frag*)(rd + ob + J * kBlk * kRowBytes);
+        if constexpr (I == kMI - 1) {
+#pragma unroll
+          for (int i = kH; i < kMI; ++i) fa[i] = *(const GEP_LDS Frag*)(rd + oa + i * kBlk * kRowBytes);
+        }
+      }
+      if constexpr (WR) dma_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave);
+      roll3_slots<WR, C0, I + 1, E>(acc, fa, fb, rd, oa, ob, la, lb, wr, src, wave);
+    }
+  }
+  // Byte offset in a stage of this lane's chunk of the 16x16 fragment of rows r0 + [0, 16),
+  // k-step s (K-major, XOR-swizzled rows).
+  static __device__ __forceinline__ int frag_off16(int r0, int s, int lane) {
+    const int row = r0 + (lane & 15);
+    return row * kRowBytes + (((s * (64 / kBlk) + (lane >> 4)) ^ kswz(row)) << 4);
+  }
+
   // One MFMA step: MFMAs on fragment buffer CUR while the fragments of k-step s of the stage
   // at `rd` are read into the other buffer; WR: register chunks [C0, C0 + kChunksPerStep)
   // are written to the stage at `wr` and reloaded from `src`. (kRoll: A in buffer 0 only.)
   template <int CUR, bool WR, int C0>
-  static __device__ __forceinline__ void step(f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI], Frag (&fb)[2][kNI],
+  static __device__ __forceinline__ void step(Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI], Frag (&fb)[2][kNI],
                                               const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
                                               const KtSrc& src, int wave, int lane, int wm0, int wn0) {
-    if constexpr (kRoll) {
+    if constexpr (kRoll3) {
+      // The fragment offsets of k-step s are made opaque: the stage, fragment and (for B)
+      // operand offsets then fold into the 16-bit immediates of the reads, one address
+      // register per operand and k-step. (Folded by the compiler, B's offsets past 64 KB took
+      // a register per fragment and stage.)
+      int oa = frag_off16(wm0, s, lane), ob = kBOff + frag_off16(wn0, s, lane);
+      asm volatile("" : "+v"(oa), "+v"(ob));
+      // Wave priority 1 for the first half of the step, 0 for the second: of the two waves
+      // sharing a SIMD, the one ahead yields to the one behind, which otherwise (the issue
+      // arbiter favours the older wave) finishes each k-tile alone while its partner waits at
+      // the barrier (8192^3 bf16: the older waves' barrier time per tile 152 K -> 99 K cycles,
+      // +2.5% throughput).
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+      roll3_slots<WR, C0, 0, kNI>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
+      sched_roll3<WR, 0, kNI>();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      roll3_slots<WR, C0, kNI, kMI>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
+      sched_roll3<WR, kNI, kMI>();
+    } else if constexpr (kRoll) {
       static_assert(kNI <= kMI, "B fragments are read in the first kNI slots");
       roll_slots<CUR, WR, C0>(acc, fa[0], fb, rd, s, la, lb, wr, src, wave, lane, wm0, wn0);
       sched_roll<WR>();
@@ -816,7 +943,7 @@ struct GemmKernel {
   // buffer S & 1 and reads k-step S+1; the first kWriteSteps steps also cycle their share of
   // the register chunks through the stage `nxt`.
   template <int S = 0, bool WRITES = true>
-  static __device__ __forceinline__ void first_steps(f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
+  static __device__ __forceinline__ void first_steps(Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
                                                      Frag (&fb)[2][kNI], const GEP_LDS char* cur, LA& la, LB& lb,
                                                      GEP_LDS char* nxt, const KtSrc& src, int wave, int lane,
                                                      int wm0, int wn0) {
@@ -829,7 +956,7 @@ struct GemmKernel {
 
   // Steps S .. E-1 of a k-tile without register chunk writes (the global -> LDS path).
   template <int S, int E>
-  static __device__ __forceinline__ void first_steps_range(f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
+  static __device__ __forceinline__ void first_steps_range(Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
                                                            Frag (&fb)[2][kNI], const GEP_LDS char* cur, LA& la, LB& lb,
                                                            GEP_LDS char* nxt, const KtSrc& src, int wave, int lane,
                                                            int wm0, int wn0) {
@@ -847,7 +974,7 @@ struct GemmKernel {
   // its reads of stage PAR returned) comes before the last step, which reads (kt+1, 0).
   template <int PAR>
   static __device__ __forceinline__ void ktile(const KParams& p, const TileInfo& ti, LA& la, LB& lb,
-                                               GEP_LDS char* smem, f32x16 (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
+                                               GEP_LDS char* smem, Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
                                                Frag (&fb)[2][kNI], int kt, int wave, int lane, int wm0, int wn0) {
     GEP_LDS char* cur = smem + PAR * kStageBytes;
     GEP_LDS char* nxt = smem + (PAR ^ 1) * kStageBytes;
@@ -871,13 +998,14 @@ struct GemmKernel {
       // yielding once ahead keeps the pair level (measured: the older waves' barrier time per
       // 256x256 tile of the 8192^3 GEMM 120 K -> 47 K cycles, +0.3-1.9% on every 8-wave
       // workload; with one wave per SIMD it changes nothing).
+      // (16x16 blocks: each step sets its own priorities)
       first_steps_range<1, kPrioSplit>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
+      if constexpr (!kRoll3) __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
       first_steps_range<kPrioSplit, kSteps - 1>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
       dma_barrier();
-      __builtin_amdgcn_s_setprio(1);
+      if constexpr (!kRoll3) __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
       step<1, true, 0>(acc, fa, fb, nxt, 0, la, lb, cur, src, wave, lane, wm0, wn0);
     } else {
@@ -888,8 +1016,9 @@ struct GemmKernel {
   }
 
   // ---- epilogue -----------------------------------------------------------------------
-  // Accumulator lane layout: for block (i, j) and register group g, lane l holds row
-  // wm0 + 32i + (l % 32) and columns wn0 + 32j + 8g + 4(l / 32) + [0, 4).
+  // Accumulator lane layout: 32x32 blocks: for block (i, j) and register group g, lane l
+  // holds row wm0 + 32i + (l % 32) and columns wn0 + 32j + 8g + 4(l / 32) + [0, 4). 16x16
+  // blocks: lane l holds row wm0 + 16i + (l % 16) and columns wn0 + 16j + 4(l / 16) + [0, 4).
   // Per pass of kBPP block rows, the wave writes its raw fp32 accumulators (straight from
   // the accumulator registers) to a row-major buffer in its share of the idle ring, then
   // reads them back 8 consecutive columns per lane, so that C loads and D / PostAct stores
@@ -899,17 +1028,23 @@ struct GemmKernel {
   // generic one.
   static constexpr int kEpiRegion = kLdsBytes / NW;
   static constexpr int kNC8 = kWN / 8;                             // 8-column groups per row
-  static constexpr int kBPP = (kEpiRegion / (32 * kWN * 4)) < kMI ? (kEpiRegion / (32 * kWN * 4)) : kMI;
+  static constexpr int kBPP = (kEpiRegion / (kBlk * kWN * 4)) < kMI ? (kEpiRegion / (kBlk * kWN * 4)) : kMI;
   static_assert(kBPP >= 1 && kMI % kBPP == 0, "epilogue passes must cover the wave tile");
   static constexpr int kRPI = 64 / kNC8;                           // rows per read instruction
-  static constexpr int kIt = kBPP * 32 / kRPI;                     // read instructions per pass
+  static constexpr int kIt = kBPP * kBlk / kRPI;                   // read instructions per pass
 
   // Byte offset of half `hf` (columns 8*c8 + 4*hf + [0, 4)) of row r in the wave's fp32
   // buffer: the first halves of all groups fill the first half of the row, the second
   // halves the second, each chunk index XOR-swizzled by the row. Acc-layout writes (32 rows,
   // one group) and row reads (one or two rows, all groups) then fall in distinct banks.
+  // (16x16 blocks with 8 groups per row: a write phase holds rows {0-3, 8-11} of one half,
+  // which the key maps to 8 distinct chunks.)
+  static __device__ __forceinline__ int ekey(int r) {
+    if constexpr (kBlk == 16 && kNC8 == 8) return (r & 3) | ((r >> 1) & 4);
+    else return r & (kNC8 - 1);
+  }
   static __device__ __forceinline__ int ebuf(int r, int c8, int hf) {
-    return r * (kWN * 4) + hf * (kWN * 2) + ((c8 ^ (r & (kNC8 - 1))) << 4);
+    return r * (kWN * 4) + hf * (kWN * 2) + ((c8 ^ ekey(r)) << 4);
   }
 
   template <int DT>
@@ -1122,13 +1257,32 @@ struct GemmKernel {
   }
 
   template <int DT, bool ACT>
-  static __device__ __forceinline__ void epilogue16(const KParams& p, const f32x16 (&acc)[kMI][kNI],
+  static __device__ __forceinline__ void epilogue16(const KParams& p, const Acc (&acc)[kMI][kNI],
                                                     GEP_LDS char* region, int lane, char* ob, int64_t ld,
                                                     int rows_valid, int cols_valid, float alpha) {
     // the LDS addresses below depend on the lane only; computed here (an opaque copy of the
     // lane id), not hoisted to the kernel's start where they would stay live, and spill,
     // across the main loop
     asm volatile("" : "+v"(lane));
+    if constexpr (kBlk == 16) {
+      // blocks j and j + 1: columns 16j + 4q + [0, 4) and the same 16 further
+      const int q = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) {
+        const int lr = i * 16 + (lane & 15);
+#pragma unroll
+        for (int j = 0; j < kNI; j += 2) {
+          const Acc& a = acc[i][j];
+          const Acc& b = acc[i][j + 1];
+          f32x8 v = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]} * alpha;
+          if constexpr (ACT) v = act8(p.act, v);
+          const i32x4 w = pack8<DT>(v);
+          *(GEP_LDS i32x2*)(region + ebuf16(lr, 2 * j + (q >> 1)) + 8 * (q & 1)) = i32x2{w[0], w[1]};
+          *(GEP_LDS i32x2*)(region + ebuf16(lr, 2 * j + 2 + (q >> 1)) + 8 * (q & 1)) = i32x2{w[2], w[3]};
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
     const int h = lane >> 5;
 #pragma unroll
     for (int i = 0; i < kMI; ++i) {
@@ -1138,7 +1292,7 @@ struct GemmKernel {
 #pragma unroll
         for (int g = 0; g < 4; g += 2) {
           // groups g, g + 1: columns 32j + 8g + 4h + [0, 4) and the same 8 further
-          const f32x16& a = acc[i][j];
+          const Acc& a = acc[i][j];
           f32x8 v = f32x8{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3],
                           a[4 * g + 4], a[4 * g + 5], a[4 * g + 6], a[4 * g + 7]} * alpha;
           if constexpr (ACT) v = act8(p.act, v);
@@ -1148,6 +1302,7 @@ struct GemmKernel {
           // one group pair at a time: keeps the converted values from crowding the registers
           __builtin_amdgcn_sched_barrier(0);
         }
+    }
     }
     asm volatile("" ::: "memory");
     const int rl = lane / kNC16, c = lane % kNC16;
@@ -1162,7 +1317,7 @@ struct GemmKernel {
   }
 
   static __device__ __forceinline__ void epilogue(const KParams& p, const TileInfo& ti,
-                                                  const f32x16 (&acc)[kMI][kNI], GEP_LDS char* region, int lane,
+                                                  const Acc (&acc)[kMI][kNI], GEP_LDS char* region, int lane,
                                                   int wm0, int wn0, float alpha, float beta) {
     const int h = lane >> 5;
     const int row0 = ti.m0 + wm0, col0 = ti.n0 + wn0;
@@ -1207,20 +1362,27 @@ struct GemmKernel {
         if (pc != pass) continue;
 #pragma unroll
         for (int ii = 0; ii < kBPP; ++ii) {
-          const int lr = ii * 32 + (lane & 31);
+          if constexpr (kBlk == 16) {
+            const int lr = ii * 16 + (lane & 15), q = lane >> 4;
 #pragma unroll
-          for (int j = 0; j < kNI; ++j)
+            for (int j = 0; j < kNI; ++j)
+              *(f32x4 GEP_LDS*)(region + ebuf(lr, 2 * j + (q >> 1), q & 1)) = acc[pc * kBPP + ii][j];
+          } else {
+            const int lr = ii * 32 + (lane & 31);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x16& a = acc[pc * kBPP + ii][j];
-              const f32x4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-              *(f32x4 GEP_LDS*)(region + ebuf(lr, 4 * j + g, h)) = v;
-            }
+            for (int j = 0; j < kNI; ++j)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const Acc& a = acc[pc * kBPP + ii][j];
+                const f32x4 v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+                *(f32x4 GEP_LDS*)(region + ebuf(lr, 4 * j + g, h)) = v;
+              }
+          }
         }
       }
       // LDS operations of one wave complete in order; keep the compiler from reordering
       asm volatile("" ::: "memory");
-      const int m0 = pass * kBPP * 32;
+      const int m0 = pass * kBPP * kBlk;
       if constexpr (DACT) {
         // (C is always present)
         if (path == 1) pass_fast<DT_BF16, true, true>(p, ea, region, m0, lane);
@@ -1248,11 +1410,13 @@ struct GemmKernel {
     volatile int32_t* next_slot = (volatile int32_t*)(smem_raw + kLdsBytes);
     const int tid = threadIdx.x, lane = tid & 63, lane_id = lane;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
-    if constexpr (NW == 8) {
+    if constexpr (NW == 8 && kBlk == 32) {
       // With two waves per SIMD a wave has 256 registers in all. An explicit AGPR operand
-      // makes the compiler split them 128 / 128 and keep the accumulators in AGPRs;
+      // makes the compiler split them 128 / 128 and keep the 32x32 accumulators in AGPRs;
       // otherwise it assumes no AGPRs and spills the 128 accumulators plus the rest of
-      // the loop state out of 256 VGPRs.
+      // the loop state out of 256 VGPRs. (16x16 accumulators stay in VGPRs, next to 12
+      // fragments: with the AGPR split the compiler moved the 4-register accumulators between
+      // the two files at every MFMA.)
       asm volatile("; accumulators live in AGPRs" ::"a"(0.f));
     }
     const int wm0 = (wave & 1) * kWM, wn0 = (wave >> 1) * kWN;
@@ -1398,11 +1562,11 @@ struct GemmKernel {
         int32_t* e = p.tile_log + ((int64_t)bid * p.tile_log_iters + iter) * 4;
         e[0] = ti.mb; e[1] = ti.nb; e[2] = ti.l; e[3] = t;
       }
-      f32x16 acc[kMI][kNI];
+      Acc acc[kMI][kNI];
 #pragma unroll
       for (int i = 0; i < kMI; ++i)
 #pragma unroll
-        for (int j = 0; j < kNI; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < kNI; ++j) acc[i][j] = Acc{};
 
       // the previous tile's epilogue buffers (and the published queue position) are free
       lds_barrier();
