@@ -5,31 +5,33 @@
 // persistent tile loop, k-tile mainloop, epi_visit_acc_subtile) and page 6,
 // quack/gemm_act_sm90.py (GemmActSm90: PostAct = act(fp32 pre-activation) next to D).
 // The design is this file's own:
-//   * 256 threads = 4 wave64s in a 2x2 grid; each wave owns a (BM/2) x (BN/2) block of the
-//     output tile, computed with v_mfma_f32_32x32x16_{f16,bf16} or, for fp8,
-//     v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales; per-operand e4m3/e5m2 format fields).
+//   * 512 threads = 8 wave64s in a 2x4 grid for 16-bit operands that are both K-major with
+//     256x256 tiles: two waves per SIMD, each owning a 128x64 block of the output tile,
+//     computed with v_mfma_f32_16x16x32_{f16,bf16}. Otherwise 256 threads = 4 wave64s in a 2x2
+//     grid, each owning a (BM/2) x (BN/2) block computed with v_mfma_f32_32x32x16_{f16,bf16}
+//     or, for fp8, v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales; per-operand e4m3/e5m2
+//     format fields).
 //   * A k-tile is 128 bytes of K per row (64 16-bit or 128 fp8 elements): every global load
-//     instruction reads whole 128-byte lines. A and B k-tiles travel global -> VGPRs
-//     (buffer_load_dwordx4, one staging register set) -> LDS (ds_write_b128) into a
-//     two-stage ring. Out-of-range rows / k-chunks use an offset past the buffer's
-//     num_records, which the hardware reads as zero (tails in M, N and K).
-//   * Each k-tile: the register set (k-tile kt+1) is written to the free stage during the
-//     first MFMA steps, every chunk reloaded from k-tile kt+2 right after its write; one
-//     barrier per k-tile, before the last MFMA step, whose fragment reads already come from
-//     the next stage.
+//     instruction reads whole 128-byte lines. A and B k-tiles go into a two-stage LDS ring,
+//     global -> LDS directly (buffer_load_dwordx4 ... lds; the 8-wave and fp8 kernels) or
+//     through a staging register set (buffer_load_dwordx4 -> ds_write_b128). Out-of-range
+//     rows / k-chunks use an offset past the buffer's num_records, which the hardware reads
+//     as zero (tails in M, N and K).
+//   * One barrier per k-tile, before the last MFMA step, whose fragment reads already come
+//     from the next stage; the transfers (or staging writes) into the stage that barrier
+//     frees follow it.
 //   * K-major tiles are stored [row][8 x 16-byte chunks] with the chunk index XOR-swizzled
-//     by the row, so the 32-row MFMA fragment reads (ds_read_b128) hit distinct banks.
-//     M/N-major (16-bit) tiles are stored [k][row] and read with ds_read_b64_tr_b16, which
-//     transposes 16x4 blocks across each 16-lane group into K-contiguous fragments.
-//   * Fragments are double-buffered in registers: the LDS reads of the next k-step are
-//     interleaved with the MFMAs of the current one.
+//     by the row, so the fragment reads (ds_read_b128) hit distinct banks. M/N-major (16-bit)
+//     tiles are stored [k][row] and read with ds_read_b64_tr_b16, which transposes 16x4
+//     blocks across each 16-lane group into K-contiguous fragments.
+//   * The LDS reads of the next k-step are interleaved with the MFMAs of the current one
+//     (double-buffered fragments, or with 8 waves a rolling set of 12).
 //   * Persistent grid: workgroup b takes tiles t = b' + i*P; t -> (m_blk, n_blk, l) by the
 //     grouped raster with FastDivmod (page 6, quack/fast_math.py); b' optionally remaps b so
 //     that the workgroups of one XCD (dispatched round-robin) take consecutive tile ids.
-//   * Epilogue: the accumulators go, 16 rows at a time, through per-wave fp32 strips in the
-//     (then idle) ring and come back row-contiguous (4 columns per lane) for scaling,
-//     beta*C, the activation, conversion and coalesced stores. The next tile's first k-tile
-//     loads are already in flight into the staging registers meanwhile.
+//   * Epilogue: the accumulators go through per-wave buffers in the (then idle) ring and come
+//     back row-contiguous (8 columns per lane) for scaling, beta*C, the activation,
+//     conversion and 16-byte stores.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -511,7 +513,7 @@ struct TileInfo {
 // VM: 0 dense batched, 1 varlen-M (cu_seqlens splits the rows), 2 varlen-K (cu_seqlens
 // splits K; one output batch per group). GA: A rows gathered through a_idx (varlen-M).
 template <int BM, int BN, int OP, int FA, int FB, bool A_K, bool B_K, int VM, int NW, bool DACT = false,
-          bool GA = false, int BLK = 0>
+          bool GA = false>
 struct GemmKernel {
   static constexpr bool VARLEN = VM == 1;
   static constexpr bool VARK = VM == 2;
@@ -520,8 +522,9 @@ struct GemmKernel {
   // NW wave64s in a 2 x (NW/2) grid over the output tile
   static constexpr int kThreads = NW * 64;
   // MFMA block: 16x16 for the 8-wave kernels (two waves per SIMD, K-major 16-bit operands),
-  // 32x32 otherwise (BLK overrides)
-  static constexpr int kBlk = BLK ? BLK : (NW == 8 ? 16 : 32);
+  // 32x32 for the 4-wave ones (whose 256 accumulators must live in AGPRs, where the compiler
+  // keeps 32x32 blocks but not 16x16 ones)
+  static constexpr int kBlk = NW == 8 ? 16 : 32;
   using Op = Mfma<OP, FA, FB, kBlk>;
   using Frag = typename Op::Frag;
   using Acc = typename Op::Acc;
@@ -561,19 +564,12 @@ struct GemmKernel {
   // MFMA steps, kCPF chunks next to each fragment read
   static constexpr int kChunksPerKt = LA::kInstr + LB::kInstr;
   static constexpr int kWriteSteps = kDMA ? 1 : (kSteps >= 4 ? 2 : 1);
-  // 16-bit global -> LDS transfers of a k-tile are issued in two halves: the first after the
-  // barrier that frees its stage, the second in the first step of the next k-tile (see ktile).
-  // fp8 keeps one: its last step holds twice the MFMA work and covers the transfers (split,
-  // fp8 8192^3 measured 8% slower). So do 16x16 blocks, whose k-tile has two steps: the
-  // second half would land in the step that ends at the barrier waiting for it (8192^3 bf16:
-  // the younger waves' barrier time per tile 77 K -> 30 K cycles with one part).
-  static constexpr int kDmaParts = (kDMA && kES == 2 && kBlk == 32) ? 2 : 1;
-  static constexpr int kChunksPerStep = kChunksPerKt / kWriteSteps / kDmaParts;
+  static constexpr int kChunksPerStep = kChunksPerKt / kWriteSteps;
   // fragment slot f carries MFMAs [mlo(f), mlo(f+1)) and register chunks [clo(f), clo(f+1))
   static constexpr int mlo(int f) { return f * kMfmaPerStep / kFrags; }
   static constexpr int clo(int f) { return f * kChunksPerStep / kFrags; }
   static_assert(kSteps % 2 == 0, "a k-tile ends on fragment buffer 0");
-  static_assert(kChunksPerKt % (kWriteSteps * kDmaParts) == 0, "register chunks must spread evenly over the write steps");
+  static_assert(kChunksPerKt % kWriteSteps == 0, "register chunks must spread evenly over the write steps");
   static_assert(kMfmaPerStep >= kFrags, "every fragment slot needs an MFMA");
 
   // ---- scheduling hints: one slot per fragment, each carrying its MFMAs, the fragment's
@@ -806,42 +802,8 @@ struct GemmKernel {
     }
   }
 
-  // ---- rolling A fragments (kRoll): one A buffer, re-read row by row. Slot i runs the
-  // MFMAs of accumulator row i, then reads A fragment i of the next k-step into the same
-  // registers (their last reader has issued), B fragment i of the next k-step (i < kNI) into
-  // the other B buffer, then cycles its register chunks. Saves kMI fragment registers, which
-  // lets two waves share a SIMD.
-  static constexpr bool kRoll = NW == 8 && kBlk == 32;
+  // register chunk / transfer range of slot i of an 8-wave step
   static constexpr int rlo(int i) { return i * kChunksPerStep / kMI; }
-  template <bool WR, int I = 0>
-  static __device__ __forceinline__ void sched_roll() {
-    if constexpr (I < kMI) {
-      constexpr int nc = rlo(I + 1) - rlo(I);
-      __builtin_amdgcn_sched_group_barrier(0x008, kNI, 0);                              // MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, kRA + (I < kNI ? kRB : 0), 0);        // LDS reads
-      if constexpr (WR && nc > 0) {
-        if constexpr (!kDMA) __builtin_amdgcn_sched_group_barrier(0x200, nc, 0);         // LDS writes
-        __builtin_amdgcn_sched_group_barrier(0x020, nc, 0);                              // VMEM loads
-      }
-      sched_roll<WR, I + 1>();
-    }
-  }
-  template <int CUR, bool WR, int C0, int I = 0>
-  static __device__ __forceinline__ void roll_slots(Acc (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[2][kNI],
-                                                    const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
-                                                    const KtSrc& src, int wave, int lane, int wm0, int wn0) {
-    if constexpr (I < kMI) {
-#pragma unroll
-      for (int j = 0; j < kNI; ++j) acc[I][j] = Op::mma(fb[CUR][j], fa[I], acc[I][j]);
-      fa[I] = read_frag<A_K, BM, Op, kPadRows>(rd, wm0 + I * kBlk, s, lane);
-      if constexpr (I < kNI) fb[CUR ^ 1][I] = read_frag<B_K, BN, Op, kPadRows>(rd + kBOff, wn0 + I * kBlk, s, lane);
-      if constexpr (WR) {
-        if constexpr (kDMA) dma_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave);
-        else cycle_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave, lane);
-      }
-      roll_slots<CUR, WR, C0, I + 1>(acc, fa, fb, rd, s, la, lb, wr, src, wave, lane, wm0, wn0);
-    }
-  }
 
   // ---- column halves (kRoll3; 16x16 blocks, kMI = 2 kNI): one A and one B buffer, 12
   // fragments live (double-buffered B with rolling A, the 32x32 scheme, needs 16 and spills
@@ -901,7 +863,8 @@ struct GemmKernel {
 
   // One MFMA step: MFMAs on fragment buffer CUR while the fragments of k-step s of the stage
   // at `rd` are read into the other buffer; WR: register chunks [C0, C0 + kChunksPerStep)
-  // are written to the stage at `wr` and reloaded from `src`. (kRoll: A in buffer 0 only.)
+  // are written to the stage at `wr` and reloaded from `src` (global -> LDS: issued to `wr`).
+  // (kRoll3: one fragment buffer, the 0 of each pair.)
   template <int CUR, bool WR, int C0>
   static __device__ __forceinline__ void step(Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI], Frag (&fb)[2][kNI],
                                               const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
@@ -928,10 +891,6 @@ struct GemmKernel {
       __builtin_amdgcn_sched_barrier(0);
       roll3_slots<WR, C0, kNI, kMI>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
       sched_roll3<WR, kNI, kMI>();
-    } else if constexpr (kRoll) {
-      static_assert(kNI <= kMI, "B fragments are read in the first kNI slots");
-      roll_slots<CUR, WR, C0>(acc, fa[0], fb, rd, s, la, lb, wr, src, wave, lane, wm0, wn0);
-      sched_roll<WR>();
     } else {
       slots<WR, C0>(fa[CUR ^ 1], fb[CUR ^ 1], rd, s, wm0, wn0, la, lb, wr, src, wave, lane);
       mma_step(acc, fa[CUR], fb[CUR]);
@@ -965,7 +924,6 @@ struct GemmKernel {
       first_steps_range<S + 1, E>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
     }
   }
-  static constexpr int kPrioSplit = kSteps - 1 < 2 ? kSteps - 1 : 2;
 
   // k-tile kt, held in stage PAR (= kt & 1); fragments (kt, 0) are in buffer 0 and the
   // staging registers hold k-tile kt+1. The first kWriteSteps steps write kt+1 into the
@@ -980,33 +938,15 @@ struct GemmKernel {
     GEP_LDS char* nxt = smem + (PAR ^ 1) * kStageBytes;
     const KtSrc src = kt_src(p, ti, kt + 2);
     if constexpr (kDMA) {
-      // Stage PAR^1 (k-tile kt+1) received the first half of its transfers in the last step of
-      // k-tile kt-1 and (16-bit) gets the second half in step 0 here (nobody reads it before
-      // this k-tile's barrier, which waits for both); k-tile kt+2 goes into stage PAR once its
-      // last fragments have been read, its first half in the last step. Issued in one step, the
-      // 64 KB of a k-tile held the transfer step at ~930-1000 cycles against 512 of MFMA work
-      // (bf16; the address path takes ~15 cycles per 1 KB instruction per CU). Same-box runs:
-      // 4096^3 with C / D / GELU PostAct +1.9%, other workloads within +-0.4% (the power-limited
-      // clock takes back the cycles saved).
-      if constexpr (kDmaParts == 2)
-        step<0, true, kChunksPerStep>(acc, fa, fb, cur, 1, la, lb, nxt, kt_src(p, ti, kt + 1), wave, lane, wm0, wn0);
-      else
-        step<0, false, 0>(acc, fa, fb, cur, 1, la, lb, nxt, src, wave, lane, wm0, wn0);
-      // The steps before kPrioSplit run at wave priority 1 (set after the previous barrier),
-      // the rest at 0: on a SIMD shared by two waves the issue arbiter favours the older wave,
-      // which otherwise runs ahead and leaves its partner to finish each k-tile alone;
-      // yielding once ahead keeps the pair level (measured: the older waves' barrier time per
-      // 256x256 tile of the 8192^3 GEMM 120 K -> 47 K cycles, +0.3-1.9% on every 8-wave
-      // workload; with one wave per SIMD it changes nothing).
-      // (16x16 blocks: each step sets its own priorities)
-      first_steps_range<1, kPrioSplit>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!kRoll3) __builtin_amdgcn_s_setprio(0);
-      __builtin_amdgcn_sched_barrier(0);
-      first_steps_range<kPrioSplit, kSteps - 1>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+      // Stage PAR^1 (k-tile kt+1) received its transfers in the last step of k-tile kt-1 and
+      // nobody reads it before this k-tile's barrier, which waits for them; k-tile kt+2 goes
+      // into stage PAR once its last fragments have been read, in the last step, one transfer
+      // per slot. (Split between the last step of kt and the first of kt+1, the second half
+      // landed just before the barrier that waits for it when a k-tile has two steps; with
+      // four 32x32 steps the split had measured +1.9% on 4096^3 with C / D / GELU PostAct,
+      // and fp8 8192^3 8% slower.)
+      first_steps_range<0, kSteps - 1>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
       dma_barrier();
-      if constexpr (!kRoll3) __builtin_amdgcn_s_setprio(1);
-      __builtin_amdgcn_sched_barrier(0);
       step<1, true, 0>(acc, fa, fb, nxt, 0, la, lb, cur, src, wave, lane, wm0, wn0);
     } else {
       first_steps(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
@@ -1410,15 +1350,6 @@ struct GemmKernel {
     volatile int32_t* next_slot = (volatile int32_t*)(smem_raw + kLdsBytes);
     const int tid = threadIdx.x, lane = tid & 63, lane_id = lane;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
-    if constexpr (NW == 8 && kBlk == 32) {
-      // With two waves per SIMD a wave has 256 registers in all. An explicit AGPR operand
-      // makes the compiler split them 128 / 128 and keep the 32x32 accumulators in AGPRs;
-      // otherwise it assumes no AGPRs and spills the 128 accumulators plus the rest of
-      // the loop state out of 256 VGPRs. (16x16 accumulators stay in VGPRs, next to 12
-      // fragments: with the AGPR split the compiler moved the 4-register accumulators between
-      // the two files at every MFMA.)
-      asm volatile("; accumulators live in AGPRs" ::"a"(0.f));
-    }
     const int wm0 = (wave & 1) * kWM, wn0 = (wave >> 1) * kWN;
 
     const int P = p.P;
