@@ -826,14 +826,16 @@ struct GemmKernel {
       sched_roll3<WR, I + 1, E>();
     }
   }
-  // slots [I, E) of a step; oa / ob: this lane's fragment offsets of the k-step read, A and B
-  template <bool WR, int C0, int I, int E>
+  // slots [I, E) of a step; oa / ob: this lane's fragment offsets of the k-step read, A and B;
+  // MM = false: only the slots' transfers (a wave whose rows all lie past the output)
+  template <bool WR, int C0, int I, int E, bool MM = true>
   static __device__ __forceinline__ void roll3_slots(Acc (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[kNI],
                                                      const GEP_LDS char* rd, int oa, int ob, LA& la, LB& lb,
                                                      GEP_LDS char* wr, const KtSrc& src, int wave) {
     static_assert(kMI == 2 * kNI && kDMA, "two halves of kNI block rows, global -> LDS transfers");
     if constexpr (I < E) {
-      if constexpr (I < kNI) {
+      if constexpr (!MM) {
+      } else if constexpr (I < kNI) {
 #pragma unroll
         for (int i = 0; i < kH; ++i) acc[i][I] = Op::mma(fb[I], fa[i], acc[i][I]);
         if constexpr (I == kNI - 1) {
@@ -851,7 +853,7 @@ struct GemmKernel {
         }
       }
       if constexpr (WR) dma_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave);
-      roll3_slots<WR, C0, I + 1, E>(acc, fa, fb, rd, oa, ob, la, lb, wr, src, wave);
+      roll3_slots<WR, C0, I + 1, E, MM>(acc, fa, fb, rd, oa, ob, la, lb, wr, src, wave);
     }
   }
   // Byte offset in a stage of this lane's chunk of the 16x16 fragment of rows r0 + [0, 16),
@@ -865,11 +867,14 @@ struct GemmKernel {
   // at `rd` are read into the other buffer; WR: register chunks [C0, C0 + kChunksPerStep)
   // are written to the stage at `wr` and reloaded from `src` (global -> LDS: issued to `wr`).
   // (kRoll3: one fragment buffer, the 0 of each pair.)
-  template <int CUR, bool WR, int C0>
+  template <int CUR, bool WR, int C0, bool MM = true>
   static __device__ __forceinline__ void step(Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI], Frag (&fb)[2][kNI],
                                               const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
                                               const KtSrc& src, int wave, int lane, int wm0, int wn0) {
-    if constexpr (kRoll3) {
+    if constexpr (!MM) {
+      static_assert(kRoll3, "only the 8-wave steps skip their MFMAs");
+      roll3_slots<WR, C0, 0, kMI, false>(acc, fa[0], fb[0], rd, 0, 0, la, lb, wr, src, wave);
+    } else if constexpr (kRoll3) {
       // The fragment offsets of k-step s are made opaque: the stage, fragment and (for B)
       // operand offsets then fold into the 16-bit immediates of the reads, one address
       // register per operand and k-step. (Folded by the compiler, B's offsets past 64 KB took
@@ -914,14 +919,14 @@ struct GemmKernel {
   }
 
   // Steps S .. E-1 of a k-tile without register chunk writes (the global -> LDS path).
-  template <int S, int E>
+  template <int S, int E, bool MM = true>
   static __device__ __forceinline__ void first_steps_range(Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
                                                            Frag (&fb)[2][kNI], const GEP_LDS char* cur, LA& la, LB& lb,
                                                            GEP_LDS char* nxt, const KtSrc& src, int wave, int lane,
                                                            int wm0, int wn0) {
     if constexpr (S < E) {
-      step<S & 1, false, S * kChunksPerStep>(acc, fa, fb, cur, S + 1, la, lb, nxt, src, wave, lane, wm0, wn0);
-      first_steps_range<S + 1, E>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+      step<S & 1, false, S * kChunksPerStep, MM>(acc, fa, fb, cur, S + 1, la, lb, nxt, src, wave, lane, wm0, wn0);
+      first_steps_range<S + 1, E, MM>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
     }
   }
 
@@ -930,7 +935,10 @@ struct GemmKernel {
   // other stage (free: its last reads were issued before the previous barrier) and reload
   // the registers with kt+2. The barrier (after lgkmcnt(0): this wave's writes landed and
   // its reads of stage PAR returned) comes before the last step, which reads (kt+1, 0).
-  template <int PAR>
+  // MM = false: the k-tile's transfers and barrier only (the 8-wave kernels' waves whose rows all
+  // lie past the output: they keep the workgroup's transfers and barriers, and leave their SIMD's
+  // MFMA pipe to their partner wave)
+  template <int PAR, bool MM = true>
   static __device__ __forceinline__ void ktile(const KParams& p, const TileInfo& ti, LA& la, LB& lb,
                                                GEP_LDS char* smem, Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
                                                Frag (&fb)[2][kNI], int kt, int wave, int lane, int wm0, int wn0) {
@@ -945,9 +953,9 @@ struct GemmKernel {
       // landed just before the barrier that waits for it when a k-tile has two steps; with
       // four 32x32 steps the split had measured +1.9% on 4096^3 with C / D / GELU PostAct,
       // and fp8 8192^3 8% slower.)
-      first_steps_range<0, kSteps - 1>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
+      first_steps_range<0, kSteps - 1, MM>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
       dma_barrier();
-      step<1, true, 0>(acc, fa, fb, nxt, 0, la, lb, cur, src, wave, lane, wm0, wn0);
+      step<1, true, 0, MM>(acc, fa, fb, nxt, 0, la, lb, cur, src, wave, lane, wm0, wn0);
     } else {
       first_steps(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
       lds_barrier();
@@ -1350,7 +1358,11 @@ struct GemmKernel {
     volatile int32_t* next_slot = (volatile int32_t*)(smem_raw + kLdsBytes);
     const int tid = threadIdx.x, lane = tid & 63, lane_id = lane;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
-    const int wm0 = (wave & 1) * kWM, wn0 = (wave >> 1) * kWN;
+    // 8 waves: waves w and w + 4, which share a SIMD, take the two row halves of one column
+    // block, so that a tile whose second row half lies past the output leaves one active wave
+    // per SIMD; 4 waves: a 2 x 2 grid
+    const int wm0 = (NW == 8 ? ((wave >> 2) & 1) : (wave & 1)) * kWM;
+    const int wn0 = (NW == 8 ? (wave & 3) : (wave >> 1)) * kWN;
 
     const int P = p.P;
     const int bid = blockIdx.x;
@@ -1499,6 +1511,10 @@ struct GemmKernel {
 #pragma unroll
         for (int j = 0; j < kNI; ++j) acc[i][j] = Acc{};
 
+      // An 8-wave wave whose rows all lie past the output (the last M-block of a varlen group,
+      // or of M) runs only the k-tiles' transfers and barriers: its SIMD partner, on the other
+      // half of the rows, then has the MFMA pipe to itself (uniform per wave).
+      const bool idle = kRoll3 && ti.m0 + wm0 >= ti.row_end;
       // the previous tile's epilogue buffers (and the published queue position) are free
       lds_barrier();
       // k-tiles, run in pairs (the stages alternate): an odd count gets one more k-tile past
@@ -1508,17 +1524,28 @@ struct GemmKernel {
         if constexpr (kDMA) {
           // k-tiles 0 and 1 -> stages 0 and 1
           dma_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 0), wave);
-          dma_chunks<0, kChunksPerStep>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);  // (half)
+          dma_chunks<0, kChunksPerKt>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);
           dma_barrier();
         } else {
           // k-tile 0 -> stage 0, registers <- k-tile 1
           cycle_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 1), wave, lane);
           lds_barrier();
         }
-        read_all(fa[0], fb[0], smem, 0, wm0, wn0, lane);
-        for (int kt = 0; kt < nk; kt += 2) {
-          ktile<0>(p, ti, la, lb, smem, acc, fa, fb, kt, wave, lane, wm0, wn0);
-          ktile<1>(p, ti, la, lb, smem, acc, fa, fb, kt + 1, wave, lane, wm0, wn0);
+        if constexpr (kRoll3) {
+          if (idle) {
+            __builtin_amdgcn_s_setprio(0);
+            for (int kt = 0; kt < nk; kt += 2) {
+              ktile<0, false>(p, ti, la, lb, smem, acc, fa, fb, kt, wave, lane, wm0, wn0);
+              ktile<1, false>(p, ti, la, lb, smem, acc, fa, fb, kt + 1, wave, lane, wm0, wn0);
+            }
+          }
+        }
+        if (!idle) {
+          read_all(fa[0], fb[0], smem, 0, wm0, wn0, lane);
+          for (int kt = 0; kt < nk; kt += 2) {
+            ktile<0>(p, ti, la, lb, smem, acc, fa, fb, kt, wave, lane, wm0, wn0);
+            ktile<1>(p, ti, la, lb, smem, acc, fa, fb, kt + 1, wave, lane, wm0, wn0);
+          }
         }
       }
 
@@ -1536,7 +1563,7 @@ struct GemmKernel {
       else lds_barrier();
       // (uniform: keeps the tile loop's state in scalar registers)
       const int tnext = ctr ? qtile(Q + __builtin_amdgcn_readfirstlane(*next_slot)) : t + P;
-      epilogue(p, ti, acc, smem + wave * kEpiRegion, lane, wm0, wn0, alpha, beta);
+      if (!idle) epilogue(p, ti, acc, smem + wave * kEpiRegion, lane, wm0, wn0, alpha, beta);
       t = tnext;
       if (t < U) begin_tile(t);
     }
