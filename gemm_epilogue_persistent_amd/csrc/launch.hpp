@@ -11,11 +11,12 @@ namespace gep {
 // over a CU's waves (one workgroup per CU); 128x128 tiles fit two per CU.
 template <int BM>
 constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
-// Waves per workgroup. 16-bit K-major x K-major 256x256 kernels (every varlen mode) run 8
-// waves (two per SIMD, 128x64 accumulators each) with global -> LDS transfers: measured +2%
-// on the 8192^3 GEMM, +4% on the 4096^3 GEMM with C and GELU, +0.5-2.5% on varlen-M (its
-// epilogue halves; the store drain moves into the next tile's first wait). Every other kernel
-// runs 4. With 8 waves and transfers the M/N-major kernels ran at half speed (batched
+// Waves per workgroup. 16-bit K-major x K-major 256x256 kernels (dense, varlen-M, gathered
+// rows, dact) run 8 waves (two per SIMD, 128x64 accumulators each, 16x16 MFMA blocks) with
+// global -> LDS transfers; on 32x32 blocks 8 waves had measured +2% on the 8192^3 GEMM, +4% on
+// the 4096^3 GEMM with C and GELU, +0.5-2.5% on varlen-M against 4 (the epilogue halves; the
+// store drain moves into the next tile's first wait). Every other kernel runs 4 (fp8: 8 waves
+// on 32x32x64 measured 4% slower). With 8 waves and transfers the M/N-major kernels ran at half speed (batched
 // 2048x2048x4096x16 550 vs 1125 TFLOP/s, varlen-K 544 vs 1108): their transposed fragment
 // reads (two ds_read_b64_tr_b16 per fragment) grow to 1.5x as many per CU with 128x64 wave
 // tiles and bound the loop.
