@@ -814,21 +814,31 @@ struct GemmKernel {
   // MFMAs before its first use. (Rows first, then columns, left the last B fragment read
   // three MFMAs before its use.)
   static constexpr bool kRoll3 = NW == 8 && kBlk == 16;
+  // transfer placement over the slots of a step, DM 0: spread (rlo); 1: the second half of a
+  // k-tile's chunks, one per slot in slots 0 .. kNI-1; 2: the first half, one per slot in
+  // slots kNI .. kMI-1
+  static constexpr int dlo(int dm, int i) {
+    return dm == 0 ? rlo(i) : (dm == 1 ? kChunksPerKt / 2 + (i < kNI ? i : kNI) : (i < kNI ? 0 : i - kNI));
+  }
+  static constexpr int dn(int dm, int i) { return dlo(dm, i + 1) - dlo(dm, i); }
+  static_assert(!kRoll3 || kChunksPerKt == 2 * kNI, "8 waves: a k-tile's transfers fill two half steps, one per slot");
   static constexpr int kH = kMI / 2;
-  template <bool WR, int I, int E>
+  template <bool WR, int I, int E, int DM = 0, bool SKIPA = false>
   static __device__ __forceinline__ void sched_roll3() {
     if constexpr (I < E) {
-      constexpr int nc = rlo(I + 1) - rlo(I);
-      constexpr int nr = I < kNI ? (I == kNI - 1 ? kH * kRA : 0) : (kRB + (I == kMI - 1 ? kH * kRA : 0));
+      constexpr int nc = dn(DM, I);
+      constexpr int nr = I < kNI ? ((I == kNI - 1 && !SKIPA) ? kH * kRA : 0) : (kRB + (I == kMI - 1 ? kH * kRA : 0));
       __builtin_amdgcn_sched_group_barrier(0x008, kH, 0);                         // MFMAs
       if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // LDS reads
       if constexpr (WR && nc > 0) __builtin_amdgcn_sched_group_barrier(0x020, nc, 0);  // transfers
-      sched_roll3<WR, I + 1, E>();
+      sched_roll3<WR, I + 1, E, DM, SKIPA>();
     }
   }
   // slots [I, E) of a step; oa / ob: this lane's fragment offsets of the k-step read, A and B;
-  // MM = false: only the slots' transfers (a wave whose rows all lie past the output)
-  template <bool WR, int C0, int I, int E, bool MM = true>
+  // MM = false: only the slots' transfers (a wave whose rows all lie past the output); DM: the
+  // transfer placement (dlo); SKIPA: slot kNI-1 leaves the re-read of its A fragments to the
+  // caller
+  template <bool WR, int C0, int I, int E, bool MM = true, int DM = 0, bool SKIPA = false>
   static __device__ __forceinline__ void roll3_slots(Acc (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[kNI],
                                                      const GEP_LDS char* rd, int oa, int ob, LA& la, LB& lb,
                                                      GEP_LDS char* wr, const KtSrc& src, int wave) {
@@ -838,7 +848,7 @@ struct GemmKernel {
       } else if constexpr (I < kNI) {
 #pragma unroll
         for (int i = 0; i < kH; ++i) acc[i][I] = Op::mma(fb[I], fa[i], acc[i][I]);
-        if constexpr (I == kNI - 1) {
+        if constexpr (I == kNI - 1 && !SKIPA) {
 #pragma unroll
           for (int i = 0; i < kH; ++i) fa[i] = *(const GEP_LDS Frag*)(rd + oa + i * kBlk * kRowBytes);
         }
@@ -852,8 +862,8 @@ struct GemmKernel {
           for (int i = kH; i < kMI; ++i) fa[i] = *(const GEP_LDS Frag*)(rd + oa + i * kBlk * kRowBytes);
         }
       }
-      if constexpr (WR) dma_chunks<C0 + rlo(I), rlo(I + 1) - rlo(I)>(la, lb, wr, src, wave);
-      roll3_slots<WR, C0, I + 1, E, MM>(acc, fa, fb, rd, oa, ob, la, lb, wr, src, wave);
+      if constexpr (WR) dma_chunks<C0 + dlo(DM, I), dn(DM, I)>(la, lb, wr, src, wave);
+      roll3_slots<WR, C0, I + 1, E, MM, DM, SKIPA>(acc, fa, fb, rd, oa, ob, la, lb, wr, src, wave);
     }
   }
   // Byte offset in a stage of this lane's chunk of the 16x16 fragment of rows r0 + [0, 16),
@@ -867,13 +877,13 @@ struct GemmKernel {
   // at `rd` are read into the other buffer; WR: register chunks [C0, C0 + kChunksPerStep)
   // are written to the stage at `wr` and reloaded from `src` (global -> LDS: issued to `wr`).
   // (kRoll3: one fragment buffer, the 0 of each pair.)
-  template <int CUR, bool WR, int C0, bool MM = true>
+  template <int CUR, bool WR, int C0, bool MM = true, int DM = 0>
   static __device__ __forceinline__ void step(Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI], Frag (&fb)[2][kNI],
                                               const GEP_LDS char* rd, int s, LA& la, LB& lb, GEP_LDS char* wr,
                                               const KtSrc& src, int wave, int lane, int wm0, int wn0) {
     if constexpr (!MM) {
       static_assert(kRoll3, "only the 8-wave steps skip their MFMAs");
-      roll3_slots<WR, C0, 0, kMI, false>(acc, fa[0], fb[0], rd, 0, 0, la, lb, wr, src, wave);
+      roll3_slots<WR, C0, 0, kMI, false, DM>(acc, fa[0], fb[0], rd, 0, 0, la, lb, wr, src, wave);
     } else if constexpr (kRoll3) {
       // The fragment offsets of k-step s are made opaque: the stage, fragment and (for B)
       // operand offsets then fold into the 16-bit immediates of the reads, one address
@@ -889,18 +899,48 @@ struct GemmKernel {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
-      roll3_slots<WR, C0, 0, kNI>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
-      sched_roll3<WR, 0, kNI>();
+      roll3_slots<WR, C0, 0, kNI, true, DM>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
+      sched_roll3<WR, 0, kNI, DM>();
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      roll3_slots<WR, C0, kNI, kMI>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
-      sched_roll3<WR, kNI, kMI>();
+      roll3_slots<WR, C0, kNI, kMI, true, DM>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
+      sched_roll3<WR, kNI, kMI, DM>();
     } else {
       slots<WR, C0>(fa[CUR ^ 1], fb[CUR ^ 1], rd, s, wm0, wn0, la, lb, wr, src, wave, lane);
       mma_step(acc, fa[CUR], fb[CUR]);
       sched_step<WR>();
     }
+  }
+
+  // The last step of an 8-wave k-tile with the k-tile barrier after its first half: that half
+  // runs on fragments read before, the barrier comes before the first read of stage `rd` (the
+  // next k-tile: the A fragments of the first block rows, taken out of slot kNI-1), and the
+  // second half issues the first half of k-tile kt+2's transfers into `wr`, whose last reads
+  // the barrier ended. MM = false: the barrier and the transfers only.
+  template <bool MM>
+  static __device__ __forceinline__ void last_step_midbar(Acc (&acc)[kMI][kNI], Frag (&fa)[2][kMI],
+                                                          Frag (&fb)[2][kNI], const GEP_LDS char* rd, LA& la, LB& lb,
+                                                          GEP_LDS char* wr, const KtSrc& src, int wave, int lane,
+                                                          int wm0, int wn0) {
+    int oa = frag_off16(wm0, 0, lane), ob = kBOff + frag_off16(wn0, 0, lane);
+    asm volatile("" : "+v"(oa), "+v"(ob));
+    if constexpr (MM) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+      roll3_slots<false, 0, 0, kNI, true, 0, true>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
+      sched_roll3<false, 0, kNI, 0, true>();
+    }
+    dma_barrier();
+    if constexpr (MM) {
+#pragma unroll
+      for (int i = 0; i < kH; ++i) fa[0][i] = *(const GEP_LDS Frag*)(rd + oa + i * kBlk * kRowBytes);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    roll3_slots<true, 0, kNI, kMI, MM, 2>(acc, fa[0], fb[0], rd, oa, ob, la, lb, wr, src, wave);
+    if constexpr (MM) sched_roll3<true, kNI, kMI, 2>();
   }
 
   // Steps S .. kSteps-2 of a k-tile (stage `cur`): step S runs the MFMAs of k-step S on
@@ -945,14 +985,22 @@ struct GemmKernel {
     GEP_LDS char* cur = smem + PAR * kStageBytes;
     GEP_LDS char* nxt = smem + (PAR ^ 1) * kStageBytes;
     const KtSrc src = kt_src(p, ti, kt + 2);
-    if constexpr (kDMA) {
-      // Stage PAR^1 (k-tile kt+1) received its transfers in the last step of k-tile kt-1 and
-      // nobody reads it before this k-tile's barrier, which waits for them; k-tile kt+2 goes
-      // into stage PAR once its last fragments have been read, in the last step, one transfer
-      // per slot. (Split between the last step of kt and the first of kt+1, the second half
-      // landed just before the barrier that waits for it when a k-tile has two steps; with
-      // four 32x32 steps the split had measured +1.9% on 4096^3 with C / D / GELU PostAct,
-      // and fp8 8192^3 8% slower.)
+    if constexpr (kRoll3) {
+      // 8 waves, two steps per k-tile. Step 0 reads the fragments of step 1 from stage PAR and
+      // issues the second half of k-tile kt+1's transfers into stage PAR^1, which received the
+      // first half in the second half of k-tile kt-1's last step. The barrier sits in the middle
+      // of the last step, before its first read of stage PAR^1; the step's second half then
+      // issues the first half of k-tile kt+2's transfers into stage PAR. Each half has at least
+      // one step to land, the address path carries transfers in both steps, and the waves of
+      // a SIMD meet at the barrier half a step later than with the barrier before the last
+      // step (8192^3 bf16 +2.5-3%, same binary, bit-identical results).
+      step<0, true, 0, MM, 1>(acc, fa, fb, cur, 1, la, lb, nxt, kt_src(p, ti, kt + 1), wave, lane, wm0, wn0);
+      last_step_midbar<MM>(acc, fa, fb, nxt, la, lb, cur, src, wave, lane, wm0, wn0);
+    } else if constexpr (kDMA) {
+      // fp8: stage PAR^1 (k-tile kt+1) received its transfers in the last step of k-tile kt-1
+      // and nobody reads it before this k-tile's barrier, which waits for them; k-tile kt+2
+      // goes into stage PAR once its last fragments have been read, in the last step (split
+      // with the first step of the next k-tile, fp8 8192^3 ran 8% slower).
       first_steps_range<0, kSteps - 1, MM>(acc, fa, fb, cur, la, lb, nxt, src, wave, lane, wm0, wn0);
       dma_barrier();
       step<1, true, 0, MM>(acc, fa, fb, nxt, 0, la, lb, cur, src, wave, lane, wm0, wn0);
@@ -1522,9 +1570,10 @@ struct GemmKernel {
       const int nk = (((ti.klen + kBK - 1) / kBK) + 1) & ~1;
       if (nk > 0) {
         if constexpr (kDMA) {
-          // k-tiles 0 and 1 -> stages 0 and 1
+          // k-tiles 0 and 1 -> stages 0 and 1 (8 waves: the first half of k-tile 1; the first
+          // k-tile's step 0 issues the rest)
           dma_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 0), wave);
-          dma_chunks<0, kChunksPerKt>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);
+          dma_chunks<0, kRoll3 ? kChunksPerKt / 2 : kChunksPerKt>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);
           dma_barrier();
         } else {
           // k-tile 0 -> stage 0, registers <- k-tile 1
