@@ -135,6 +135,20 @@ struct Mfma<OP_FP8, FA, FB, 32> {
   }
 };
 
+// 16x16x128 (the 8-wave fp8 kernels): zero scale operands make the compiler emit the
+// unscaled instruction, which needs no register for them.
+template <int FA, int FB>
+struct Mfma<OP_FP8, FA, FB, 16> {
+  static constexpr int kES = 1;
+  static constexpr int kKStep = 128;
+  static constexpr int kBlk = 16;
+  using Frag = i32x8;
+  using Acc = f32x4;
+  static __device__ __forceinline__ Acc mma(Frag b, Frag a, Acc c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, FB, FA, 0, 0, 0, 0);
+  }
+};
+
 // ------------------------------------------------------------------------------------
 // LDS tile layouts
 // ------------------------------------------------------------------------------------
@@ -568,7 +582,7 @@ struct GemmKernel {
   // fragment slot f carries MFMAs [mlo(f), mlo(f+1)) and register chunks [clo(f), clo(f+1))
   static constexpr int mlo(int f) { return f * kMfmaPerStep / kFrags; }
   static constexpr int clo(int f) { return f * kChunksPerStep / kFrags; }
-  static_assert(kSteps % 2 == 0, "a k-tile ends on fragment buffer 0");
+  static_assert(kSteps % 2 == 0 || (NW == 8 && kSteps == 1), "a k-tile ends on fragment buffer 0");
   static_assert(kChunksPerKt % kWriteSteps == 0, "register chunks must spread evenly over the write steps");
   static_assert(kMfmaPerStep >= kFrags, "every fragment slot needs an MFMA");
 
@@ -813,7 +827,7 @@ struct GemmKernel {
   // rows are re-read at the end. Every fragment of the next k-step is read at least kNI * kH
   // MFMAs before its first use. (Rows first, then columns, left the last B fragment read
   // three MFMAs before its use.)
-  static constexpr bool kRoll3 = NW == 8 && kBlk == 16;
+  static constexpr bool kRoll3 = NW == 8 && kBlk == 16 && kSteps >= 2;
   // transfer placement over the slots of a step, DM 0: spread (rlo); 1: the second half of a
   // k-tile's chunks, one per slot in slots 0 .. kNI-1; 2: the first half, one per slot in
   // slots kNI .. kMI-1
@@ -943,6 +957,130 @@ struct GemmKernel {
     if constexpr (MM) sched_roll3<true, kNI, kMI, 2>();
   }
 
+  // ---- 8 waves, one k-step per k-tile (fp8: a 16x16x128 instruction takes all 128 bytes of
+  // K of a k-tile). A fragment is 8 registers, too many for the 12 fragments of the column
+  // halves next to the 128 accumulators; this loop keeps 6: the 4 B fragments and a ring of 2
+  // A fragments (block row r in register r & 1). The 32 MFMAs run row by row, position p
+  // being block row p / kNI, column p % kNI. The A fragment of row r >= 2 is read right after
+  // the last MFMA of row r-2 (row 1 after the first MFMA), 5 MFMAs before its first use. The
+  // k-tile barrier precedes the last row: by then every wave has read its last fragment of
+  // this k-tile's stage. After it, the first MFMA of the last row is followed by the read of
+  // the next k-tile's row-0 A fragment, and each MFMA by that k-tile's B fragment of its
+  // column: 4 MFMAs before their first use. A k-tile's 8 transfers go out in two halves: one
+  // per MFMA of the last row of the k-tile two before it (into the stage its barrier freed),
+  // and one per two MFMAs over the first two rows of the k-tile before it, landing before that
+  // k-tile's barrier. Positions [0, kPrioP) run at wave priority 1.
+  static constexpr bool kStream = NW == 8 && kSteps == 1;
+  static constexpr int kLastP = kMfmaPerStep - kNI;  // first position of the last block row
+  static constexpr int kHalfKt = kChunksPerKt / 2;
+  static constexpr int kPrioP = kLastP / 2;
+  static_assert(!kStream || (kMI >= 4 && kHalfKt == kNI && 2 * kHalfKt <= kLastP),
+                "one transfer per MFMA of the last row, one per two over the first rows");
+  // rows of this k-tile whose A fragments are read after position p (bit r)
+  static constexpr int s_rd_cur(int p) {
+    int m = 0;
+    for (int r = 1; r < kMI; ++r) m |= ((r == 1 ? 0 : (r - 1) * kNI - 1) == p) << r;
+    return m;
+  }
+  static constexpr int s_nreads(int p) { return 2 * (popc(s_rd_cur(p)) + (p == kLastP) + (p >= kLastP)); }
+  static constexpr int popc(int m) { return m ? (m & 1) + popc(m >> 1) : 0; }
+  static constexpr bool s_head_dma(int p) { return p % 2 == 0 && p < 2 * kHalfKt; }
+
+  // a fragment from its two 16-byte halves (lane offsets o0, o1 from the block-row base)
+  static __device__ __forceinline__ Frag s_frag(const GEP_LDS char* base, int o0, int o1) {
+    const i32x4 lo = *(const GEP_LDS i32x4*)(base + o0);
+    const i32x4 hi = *(const GEP_LDS i32x4*)(base + o1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  template <int M, int R = 0>
+  static __device__ __forceinline__ void s_read_rows(Frag (&fa)[kMI], const GEP_LDS char* st, int o0, int o1) {
+    if constexpr (R < kMI) {
+      if constexpr ((M >> R) & 1) fa[R & 1] = s_frag(st + R * kBlk * kRowBytes, o0, o1);
+      s_read_rows<M, R + 1>(fa, st, o0, o1);
+    }
+  }
+  // Positions [P, E) of k-tile kt: stage `cur` holds kt and receives the last row's transfers
+  // of kt+2 (from s2); stage `nxt` holds kt+1, whose second half the first rows issue (from
+  // s1). MM = false: the transfers only.
+  template <bool MM, int P, int E>
+  static __device__ __forceinline__ void s_run(Acc (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[kNI],
+                                               GEP_LDS char* cur, GEP_LDS char* nxt, int oa0, int oa1, int ob0,
+                                               int ob1, LA& la, LB& lb, const KtSrc& s1, const KtSrc& s2, int wave) {
+    if constexpr (P < E) {
+      if constexpr (MM) {
+        constexpr int r = P / kNI, c = P % kNI;
+        acc[r][c] = Op::mma(fb[c], fa[r & 1], acc[r][c]);
+        s_read_rows<s_rd_cur(P)>(fa, cur, oa0, oa1);
+        if constexpr (P == kLastP) fa[0] = s_frag(nxt, oa0, oa1);
+        if constexpr (P >= kLastP) fb[P - kLastP] = s_frag(nxt + (P - kLastP) * kBlk * kRowBytes, ob0, ob1);
+      }
+      if constexpr (s_head_dma(P)) dma_chunks<kHalfKt + P / 2, 1>(la, lb, nxt, s1, wave);
+      if constexpr (P >= kLastP) dma_chunks<P - kLastP, 1>(la, lb, cur, s2, wave);
+      s_run<MM, P + 1, E>(acc, fa, fb, cur, nxt, oa0, oa1, ob0, ob1, la, lb, s1, s2, wave);
+    }
+  }
+  template <int P, int E>
+  static __device__ __forceinline__ void s_sched() {
+    if constexpr (P < E) {
+      constexpr int nt = s_head_dma(P) + (P >= kLastP);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
+      if constexpr (s_nreads(P) > 0) __builtin_amdgcn_sched_group_barrier(0x100, s_nreads(P), 0);  // LDS reads
+      if constexpr (nt > 0) __builtin_amdgcn_sched_group_barrier(0x020, nt, 0);                  // transfers
+      s_sched<P + 1, E>();
+    }
+  }
+  // Lane offsets of the two 16-byte halves of a lane's fragment in block row r0: row
+  // r0 + (l % 16), K chunks l / 16 and l / 16 + 4. A and B take the same K assignment, so the
+  // MFMA sums the same products; chunks l / 16 + {0, 4} (rather than 2 (l / 16) + {0, 1})
+  // keep the 16 rows of a read phase on distinct banks.
+  static __device__ __forceinline__ void s_offs(int r0, int lane, int& o0, int& o1) {
+    const int row = r0 + (lane & 15);
+    o0 = row * kRowBytes + (((lane >> 4) ^ kswz(row)) << 4);
+    o1 = o0 ^ 64;
+  }
+  // the fragments a tile's first k-tile starts with: all of B, and A's block row 0
+  static __device__ __forceinline__ void s_first(Frag (&fa)[kMI], Frag (&fb)[kNI], const GEP_LDS char* st, int lane,
+                                                 int wm0, int wn0) {
+    int oa0, oa1, ob0, ob1;
+    s_offs(wm0, lane, oa0, oa1);
+    s_offs(wn0, lane, ob0, ob1);
+    fa[0] = s_frag(st, oa0, oa1);
+#pragma unroll
+    for (int c = 0; c < kNI; ++c) fb[c] = s_frag(st + kBOff + c * kBlk * kRowBytes, ob0, ob1);
+  }
+  template <bool MM>
+  static __device__ __forceinline__ void s_ktile(Acc (&acc)[kMI][kNI], Frag (&fa)[kMI], Frag (&fb)[kNI],
+                                                 GEP_LDS char* cur, GEP_LDS char* nxt, LA& la, LB& lb, const KtSrc& s1,
+                                                 const KtSrc& s2, int wave, int lane, int wm0, int wn0) {
+    // opaque offsets: stage, block-row and (B) operand offsets fold into the reads' immediates
+    int oa0, oa1, ob0, ob1;
+    s_offs(wm0, lane, oa0, oa1);
+    s_offs(wn0, lane, ob0, ob1);
+    ob0 += kBOff;
+    ob1 += kBOff;
+    asm volatile("" : "+v"(oa0), "+v"(oa1), "+v"(ob0), "+v"(ob1));
+    if constexpr (MM) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+      s_run<true, 0, kPrioP>(acc, fa, fb, cur, nxt, oa0, oa1, ob0, ob1, la, lb, s1, s2, wave);
+      s_sched<0, kPrioP>();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      s_run<true, kPrioP, kLastP>(acc, fa, fb, cur, nxt, oa0, oa1, ob0, ob1, la, lb, s1, s2, wave);
+      s_sched<kPrioP, kLastP>();
+      dma_barrier();
+      s_run<true, kLastP, kMfmaPerStep>(acc, fa, fb, cur, nxt, oa0, oa1, ob0, ob1, la, lb, s1, s2, wave);
+      s_sched<kLastP, kMfmaPerStep>();
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      s_run<false, 0, kLastP>(acc, fa, fb, cur, nxt, oa0, oa1, ob0, ob1, la, lb, s1, s2, wave);
+      dma_barrier();
+      s_run<false, kLastP, kMfmaPerStep>(acc, fa, fb, cur, nxt, oa0, oa1, ob0, ob1, la, lb, s1, s2, wave);
+    }
+  }
+
   // Steps S .. kSteps-2 of a k-tile (stage `cur`): step S runs the MFMAs of k-step S on
   // buffer S & 1 and reads k-step S+1; the first kWriteSteps steps also cycle their share of
   // the register chunks through the stage `nxt`.
@@ -985,7 +1123,9 @@ struct GemmKernel {
     GEP_LDS char* cur = smem + PAR * kStageBytes;
     GEP_LDS char* nxt = smem + (PAR ^ 1) * kStageBytes;
     const KtSrc src = kt_src(p, ti, kt + 2);
-    if constexpr (kRoll3) {
+    if constexpr (kStream) {
+      s_ktile<MM>(acc, fa[0], fb[0], cur, nxt, la, lb, kt_src(p, ti, kt + 1), src, wave, lane, wm0, wn0);
+    } else if constexpr (kRoll3) {
       // 8 waves, two steps per k-tile. Step 0 reads the fragments of step 1 from stage PAR and
       // issues the second half of k-tile kt+1's transfers into stage PAR^1, which received the
       // first half in the second half of k-tile kt-1's last step. The barrier sits in the middle
@@ -1562,7 +1702,7 @@ struct GemmKernel {
       // An 8-wave wave whose rows all lie past the output (the last M-block of a varlen group,
       // or of M) runs only the k-tiles' transfers and barriers: its SIMD partner, on the other
       // half of the rows, then has the MFMA pipe to itself (uniform per wave).
-      const bool idle = kRoll3 && ti.m0 + wm0 >= ti.row_end;
+      const bool idle = (kRoll3 || kStream) && ti.m0 + wm0 >= ti.row_end;
       // the previous tile's epilogue buffers (and the published queue position) are free
       lds_barrier();
       // k-tiles, run in pairs (the stages alternate): an odd count gets one more k-tile past
@@ -1573,14 +1713,14 @@ struct GemmKernel {
           // k-tiles 0 and 1 -> stages 0 and 1 (8 waves: the first half of k-tile 1; the first
           // k-tile's step 0 issues the rest)
           dma_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 0), wave);
-          dma_chunks<0, kRoll3 ? kChunksPerKt / 2 : kChunksPerKt>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);
+          dma_chunks<0, (kRoll3 || kStream) ? kChunksPerKt / 2 : kChunksPerKt>(la, lb, smem + kStageBytes, kt_src(p, ti, 1), wave);
           dma_barrier();
         } else {
           // k-tile 0 -> stage 0, registers <- k-tile 1
           cycle_chunks<0, kChunksPerKt>(la, lb, smem, kt_src(p, ti, 1), wave, lane);
           lds_barrier();
         }
-        if constexpr (kRoll3) {
+        if constexpr (kRoll3 || kStream) {
           if (idle) {
             __builtin_amdgcn_s_setprio(0);
             for (int kt = 0; kt < nk; kt += 2) {
@@ -1590,7 +1730,8 @@ struct GemmKernel {
           }
         }
         if (!idle) {
-          read_all(fa[0], fb[0], smem, 0, wm0, wn0, lane);
+          if constexpr (kStream) s_first(fa[0], fb[0], smem, lane, wm0, wn0);
+          else read_all(fa[0], fb[0], smem, 0, wm0, wn0, lane);
           for (int kt = 0; kt < nk; kt += 2) {
             ktile<0>(p, ti, la, lb, smem, acc, fa, fb, kt, wave, lane, wm0, wn0);
             ktile<1>(p, ti, la, lb, smem, acc, fa, fb, kt + 1, wave, lane, wm0, wn0);

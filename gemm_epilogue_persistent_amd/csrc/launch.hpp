@@ -11,17 +11,18 @@ namespace gep {
 // over a CU's waves (one workgroup per CU); 128x128 tiles fit two per CU.
 template <int BM>
 constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
-// Waves per workgroup. 16-bit K-major x K-major 256x256 kernels (dense, varlen-M, gathered
-// rows, dact) run 8 waves (two per SIMD, 128x64 accumulators each, 16x16 MFMA blocks) with
-// global -> LDS transfers; on 32x32 blocks 8 waves had measured +2% on the 8192^3 GEMM, +4% on
-// the 4096^3 GEMM with C and GELU, +0.5-2.5% on varlen-M against 4 (the epilogue halves; the
-// store drain moves into the next tile's first wait). Every other kernel runs 4 (fp8: 8 waves
-// on 32x32x64 measured 4% slower). With 8 waves and transfers the M/N-major kernels ran at half speed (batched
-// 2048x2048x4096x16 550 vs 1125 TFLOP/s, varlen-K 544 vs 1108): their transposed fragment
-// reads (two ds_read_b64_tr_b16 per fragment) grow to 1.5x as many per CU with 128x64 wave
-// tiles and bound the loop.
+// Waves per workgroup. K-major x K-major 256x256 kernels (16-bit: dense, varlen-M, gathered
+// rows, dact; fp8: all) run 8 waves (two per SIMD, 128x64 accumulators each, 16x16 MFMA
+// blocks) with global -> LDS transfers; on 32x32 blocks 8 waves had measured +2% on the 8192^3
+// GEMM, +4% on the 4096^3 GEMM with C and GELU, +0.5-2.5% on varlen-M against 4 (the epilogue
+// halves; the store drain moves into the next tile's first wait); fp8 on 16x16x128 blocks
+// +3% on 8192^3 against 4 waves on 32x32x64 (on 32x32x64, 8 waves had been 4% slower). Every
+// other kernel runs 4. With 8 waves and transfers the M/N-major kernels ran at half speed
+// (batched 2048x2048x4096x16 550 vs 1125 TFLOP/s, varlen-K 544 vs 1108): their transposed
+// fragment reads (two ds_read_b64_tr_b16 per fragment) grow to 1.5x as many per CU with
+// 128x64 wave tiles and bound the loop.
 template <int BM, int OP, bool AK, bool BK>
-constexpr int waves() { return (BM == 256 && OP != OP_FP8 && AK && BK) ? 8 : 4; }
+constexpr int waves() { return (BM == 256 && AK && BK) ? 8 : 4; }
 
 // VM: 0 dense batched, 1 varlen-M, 2 varlen-K. DA: the activation-backward epilogue (its own
 // instantiations, so that the forward kernels carry none of its code or registers). GA: A read
