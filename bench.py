@@ -179,7 +179,7 @@ def time_plan(plan, args, steps, warmup, settle_s=0.0):
 
 def mfma_ceiling(dtype, peak, reps=3):
     """The MFMA rate probe (gemm_epilogue_persistent_amd.measure): pure MFMA loops on uniform
-    [-1, 1) operands held in registers, one workgroup per CU (4 waves; 8 for the 16x16 form),
+    [-1, 1) operands held in registers, one workgroup per CU (4 waves; 8 for the 16x16 forms),
     no memory traffic. Returns the sustained rate and the shader clock it ran at (cycles over
     the 100 MHz real-time counter)."""
     import statistics
@@ -187,10 +187,12 @@ def mfma_ceiling(dtype, peak, reps=3):
     from gemm_epilogue_persistent_amd.measure import probe_mfma
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
-    iters = 10000 if dtype == "e4m3" else 20000
+    iters = 10000 if dtype.startswith("e4m3") else 20000
     # FLOPs per wave per iteration, waves per workgroup
     if dtype == "bf16_16x16":
         flop_iter, waves = 32 * 2 * 16 * 16 * 32, 8
+    elif dtype == "e4m3_16x16":
+        flop_iter, waves = 32 * 2 * 16 * 16 * 128, 8
     else:
         flop_iter, waves = 16 * 2 * 32 * 32 * (16 if dtype == "bf16" else 64), 4
     stream = torch.cuda.current_stream()
@@ -324,16 +326,18 @@ def main():
     del args, plan
     if not a.no_ceiling:
         # the practical MFMA ceiling on full-entropy data at the clock the part sustains
-        ceil = {d: mfma_ceiling(d, PEAK_TFLOPS["e4m3" if d == "e4m3" else "bf16"])
-                for d in ("bf16", "bf16_16x16", "e4m3")}
+        ceil = {d: mfma_ceiling(d, PEAK_TFLOPS["e4m3" if d.startswith("e4m3") else "bf16"])
+                for d in ("bf16", "bf16_16x16", "e4m3", "e4m3_16x16")}
         progress(f"MFMA ceiling probe: {ceil['bf16']['tflops']} (bf16 32x32), {ceil['bf16_16x16']['tflops']} "
-                 f"(bf16 16x16), {ceil['e4m3']['tflops']} (fp8) TFLOP/s")
+                 f"(bf16 16x16), {ceil['e4m3']['tflops']} (fp8 32x32), {ceil['e4m3_16x16']['tflops']} "
+                 f"(fp8 16x16) TFLOP/s")
         out["mfma_ceiling"] = ceil
         # the form the workload's kernel issues: 16x16 in the 8-wave kernels (256x256 tiles,
-        # both operands K-major, 16-bit), 32x32 elsewhere
+        # both operands K-major), 32x32 elsewhere
         kmajor = inp.A.stride(-1) == 1 and inp.B.stride(-1) == 1
-        form = ("e4m3" if inp.a_dt in ("e4m3", "e5m2")
-                else ("bf16_16x16" if tm == 256 and kmajor else "bf16"))
+        w8 = tm == 256 and kmajor
+        form = (("e4m3_16x16" if w8 else "e4m3") if inp.a_dt in ("e4m3", "e5m2")
+                else ("bf16_16x16" if w8 else "bf16"))
         c = ceil[form]
         roof["mfma_form"] = form
         roof["frac_of_mfma_ceiling"] = round(tflops / c["tflops"], 4)

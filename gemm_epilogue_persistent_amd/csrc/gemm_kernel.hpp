@@ -129,14 +129,14 @@ struct Mfma<OP_FP8, FA, FB, 32> {
   using Frag = i32x8;
   using Acc = f32x16;
   // cbsz / blgp select the format of the first / second source (0 = e4m3, 1 = e5m2):
-  // B's format goes in cbsz and A's in blgp. Scales of 127 are 2^0 in E8M0 (no scaling).
+  // B's format goes in cbsz and A's in blgp. Zero scale operands make the compiler emit the
+  // unscaled instruction, which needs no register for them.
   static __device__ __forceinline__ Acc mma(Frag b, Frag a, Acc c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, FB, FA, 0, 0, 0, 0);
   }
 };
 
-// 16x16x128 (the 8-wave fp8 kernels): zero scale operands make the compiler emit the
-// unscaled instruction, which needs no register for them.
+// 16x16x128 (the 8-wave fp8 kernels), the same way
 template <int FA, int FB>
 struct Mfma<OP_FP8, FA, FB, 16> {
   static constexpr int kES = 1;

@@ -8,7 +8,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmfma_probe.so")
-_DT = {"bf16": 0, "e4m3": 1, "bf16_16x16": 2}
+_DT = {"bf16": 0, "e4m3": 1, "bf16_16x16": 2, "e4m3_16x16": 3}
 _lib = None
 
 

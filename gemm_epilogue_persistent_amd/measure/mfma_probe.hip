@@ -1,7 +1,7 @@
 // MFMA rate probe: measurement support for the benchmark's roofline, built into its own
 // library (libmfma_probe.so), apart from the GEMM library. One workgroup per compute unit
-// (4 waves, or 8 for the 16x16 form: two per SIMD, as in the GEMM kernels that use it) issues
-// back-to-back independent MFMAs on full-entropy operands in registers, with no memory
+// (4 waves, or 8 for the 16x16 forms: two per SIMD, as in the GEMM kernels that use them)
+// issues back-to-back independent MFMAs on full-entropy operands in registers, with no memory
 // traffic, and records its shader-clock and real-time cycle counts. On a
 // power-limited part the rate such a loop sustains with random operands is the practical
 // ceiling of any GEMM kernel on the same data; the clock it settles at is reported with it.
@@ -10,7 +10,7 @@
 
 namespace probe {
 
-enum { OP_BF16 = 0, OP_FP8 = 1, OP_BF16_16 = 2 };  // the dtype codes of mfma_probe_run
+enum { OP_BF16 = 0, OP_FP8 = 1, OP_BF16_16 = 2, OP_FP8_16 = 3 };  // the dtype codes of mfma_probe_run
 
 typedef __bf16 pbf16x8 __attribute__((ext_vector_type(8)));
 typedef float pf32x16 __attribute__((ext_vector_type(16)));
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256, 1) void mfma_probe_kernel(int iters, uint32_t 
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int j = 0; j < 16; ++j)
-        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j & 3], a[j >> 2], acc[j], 0, 0, 0, 127, 0, 127);
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j & 3], a[j >> 2], acc[j], 0, 0, 0, 0, 0, 0);
     }
   } else {
     pbf16x8 a[4], b[4];
@@ -117,25 +117,70 @@ __global__ __launch_bounds__(512, 1) void mfma_probe16_kernel(int iters, uint32_
   if (sum == 1.2345e-30f) out[0] = -1;  // keeps the accumulators live
 }
 
+// v_mfma_f32_16x16x128_f8f6f4 (zero scale operands: the unscaled instruction, as in the GEMM
+// kernels): 8 waves, each with 8 x 4 independent 16x16 blocks, e4m3 operands.
+__global__ __launch_bounds__(512, 1) void mfma_probe16_fp8_kernel(int iters, uint32_t seed, int64_t* out) {
+  uint32_t st = seed ^ (blockIdx.x * 512u + threadIdx.x) * 2654435761u;
+  for (int i = 0; i < 4; ++i) lcg(st);
+  pi32x8 a[8], b[4];
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(unit(st), unit(st), 0, false);
+      a[f][w] = __builtin_amdgcn_cvt_pk_fp8_f32(unit(st), unit(st), lo, true);
+    }
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(unit(st), unit(st), 0, false);
+      b[f][w] = __builtin_amdgcn_cvt_pk_fp8_f32(unit(st), unit(st), lo, true);
+    }
+  pf32x4 acc[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) acc[j] = pf32x4{};
+  const int64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b[j & 3], a[j >> 2], acc[j], 0, 0, 0, 0, 0, 0);
+  }
+  const int64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum += acc[j][e];
+  if (threadIdx.x == 0) {
+    out[blockIdx.x * 2] = t1 - t0;
+    out[blockIdx.x * 2 + 1] = r1 - r0;
+  }
+  if (sum == 1.2345e-30f) out[0] = -1;  // keeps the accumulators live
+}
+
 }  // namespace probe
 
 // Launch `blocks` workgroups, each wave issuing iters x 16 independent MFMAs (dtype 0:
 // v_mfma_f32_32x32x16_bf16; 1: the 32x32x64 fp8 form, e4m3 operands; 4 waves per workgroup)
-// or iters x 32 (dtype 2: v_mfma_f32_16x16x32_bf16, 8 waves per workgroup) on uniform
-// [-1, 1) operands drawn in registers from `seed`. Workgroup b writes int64 {shader-clock
-// cycles, 100 MHz real-time ticks} of its loop to out_dev[2b], out_dev[2b+1] (a device buffer
-// of 2 * blocks int64, owned by the caller). Asynchronous on `stream`. Returns 0 on success,
+// or iters x 32 (dtype 2: v_mfma_f32_16x16x32_bf16; 3: the 16x16x128 fp8 form, e4m3
+// operands; 8 waves per workgroup) on uniform [-1, 1) operands drawn in registers from
+// `seed`. Workgroup b writes int64 {shader-clock cycles, 100 MHz real-time ticks} of its
+// loop to out_dev[2b], out_dev[2b+1] (a device buffer of 2 * blocks int64, owned by the
+// caller). Asynchronous on `stream`. Returns 0 on success,
 // 1 for a bad argument (iters or blocks <= 0, NULL buffer, unknown dtype), 2 if the launch
 // fails.
 extern "C" int mfma_probe_run(int32_t dtype, int32_t iters, uint32_t seed, int32_t blocks, int64_t* out_dev,
                               void* stream) {
-  if (iters <= 0 || blocks <= 0 || !out_dev || dtype < probe::OP_BF16 || dtype > probe::OP_BF16_16) return 1;
+  if (iters <= 0 || blocks <= 0 || !out_dev || dtype < probe::OP_BF16 || dtype > probe::OP_FP8_16) return 1;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == probe::OP_BF16)
     hipLaunchKernelGGL(probe::mfma_probe_kernel<probe::OP_BF16>, dim3(blocks), dim3(256), 0, s, iters, seed, out_dev);
   else if (dtype == probe::OP_FP8)
     hipLaunchKernelGGL(probe::mfma_probe_kernel<probe::OP_FP8>, dim3(blocks), dim3(256), 0, s, iters, seed, out_dev);
-  else
+  else if (dtype == probe::OP_BF16_16)
     hipLaunchKernelGGL(probe::mfma_probe16_kernel, dim3(blocks), dim3(512), 0, s, iters, seed, out_dev);
+  else
+    hipLaunchKernelGGL(probe::mfma_probe16_fp8_kernel, dim3(blocks), dim3(512), 0, s, iters, seed, out_dev);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

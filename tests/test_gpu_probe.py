@@ -8,7 +8,7 @@ from gemm_epilogue_persistent_amd.measure import probe_mfma
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "e4m3", "bf16_16x16"])
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3", "bf16_16x16", "e4m3_16x16"])
 def test_probe_reports_cycles(dtype):
     blocks = 8
     out = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
