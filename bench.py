@@ -34,13 +34,40 @@ SECONDARY = ["fp8_8192", "varlen_moe", "square_8192_f16", "act_4096", "batched_2
              "varlen_k_moe", "varlen_moe_gather", "varlen_k_moe_gather"]
 
 
+def code_text(src):
+    """C++ source without its comments, one token run per line: what a comment or layout edit
+    leaves unchanged."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(" ".join(line.split()) for line in "".join(out).splitlines() if line.strip())
+
+
 def source_hash():
-    """Hash of the kernel sources: traffic counters are only reported for the same code."""
+    """Hash of the kernel sources' code (comments and layout excluded): traffic counters are
+    only reported for the same code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gemm_epilogue_persistent_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(f.encode() + b"\0")
+            h.update(code_text(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

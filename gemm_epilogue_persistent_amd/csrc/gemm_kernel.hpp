@@ -5,27 +5,28 @@
 // persistent tile loop, k-tile mainloop, epi_visit_acc_subtile) and page 6,
 // quack/gemm_act_sm90.py (GemmActSm90: PostAct = act(fp32 pre-activation) next to D).
 // The design is this file's own:
-//   * 512 threads = 8 wave64s in a 2x4 grid for 16-bit operands that are both K-major with
-//     256x256 tiles: two waves per SIMD, each owning a 128x64 block of the output tile,
-//     computed with v_mfma_f32_16x16x32_{f16,bf16}. Otherwise 256 threads = 4 wave64s in a 2x2
-//     grid, each owning a (BM/2) x (BN/2) block computed with v_mfma_f32_32x32x16_{f16,bf16}
-//     or, for fp8, v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales; per-operand e4m3/e5m2
-//     format fields).
+//   * 512 threads = 8 wave64s in a 2x4 grid for operands that are both K-major with 256x256
+//     tiles: two waves per SIMD, each owning a 128x64 block of the output tile, computed with
+//     v_mfma_f32_16x16x32_{f16,bf16} or v_mfma_f32_16x16x128_f8f6f4. Otherwise 256 threads =
+//     4 wave64s in a 2x2 grid, each owning a (BM/2) x (BN/2) block computed with
+//     v_mfma_f32_32x32x16_{f16,bf16} or v_mfma_f32_32x32x64_f8f6f4 (fp8: per-operand
+//     e4m3/e5m2 format fields, no scaling).
 //   * A k-tile is 128 bytes of K per row (64 16-bit or 128 fp8 elements): every global load
 //     instruction reads whole 128-byte lines. A and B k-tiles go into a two-stage LDS ring,
 //     global -> LDS directly (buffer_load_dwordx4 ... lds; the 8-wave and fp8 kernels) or
 //     through a staging register set (buffer_load_dwordx4 -> ds_write_b128). Out-of-range
 //     rows / k-chunks use an offset past the buffer's num_records, which the hardware reads
 //     as zero (tails in M, N and K).
-//   * One barrier per k-tile, before the last MFMA step, whose fragment reads already come
-//     from the next stage; the transfers (or staging writes) into the stage that barrier
-//     frees follow it.
+//   * One barrier per k-tile, placed before the first fragment read from the next stage
+//     (before the last MFMA step, or inside it with 8 waves); the transfers (or staging
+//     writes) into the stage that barrier frees follow it.
 //   * K-major tiles are stored [row][8 x 16-byte chunks] with the chunk index XOR-swizzled
 //     by the row, so the fragment reads (ds_read_b128) hit distinct banks. M/N-major (16-bit)
 //     tiles are stored [k][row] and read with ds_read_b64_tr_b16, which transposes 16x4
 //     blocks across each 16-lane group into K-contiguous fragments.
 //   * The LDS reads of the next k-step are interleaved with the MFMAs of the current one
-//     (double-buffered fragments, or with 8 waves a rolling set of 12).
+//     (double-buffered fragments; with 8 waves a rolling set of 12, or for fp8 the 4 B
+//     fragments and a ring of 2 A fragments).
 //   * Persistent grid: workgroup b takes tiles t = b' + i*P; t -> (m_blk, n_blk, l) by the
 //     grouped raster with FastDivmod (page 6, quack/fast_math.py); b' optionally remaps b so
 //     that the workgroups of one XCD (dispatched round-robin) take consecutive tile ids.
@@ -535,8 +536,8 @@ struct GemmKernel {
   static constexpr bool GAK = GA && VARK;  // gathered k-rows of A
   // NW wave64s in a 2 x (NW/2) grid over the output tile
   static constexpr int kThreads = NW * 64;
-  // MFMA block: 16x16 for the 8-wave kernels (two waves per SIMD, K-major 16-bit operands),
-  // 32x32 for the 4-wave ones (whose 256 accumulators must live in AGPRs, where the compiler
+  // MFMA block: 16x16 for the 8-wave kernels (two waves per SIMD, K-major operands), 32x32
+  // for the 4-wave ones (whose 256 accumulators must live in AGPRs, where the compiler
   // keeps 32x32 blocks but not 16x16 ones)
   static constexpr int kBlk = NW == 8 ? 16 : 32;
   using Op = Mfma<OP, FA, FB, kBlk>;
@@ -544,11 +545,11 @@ struct GemmKernel {
   using Acc = typename Op::Acc;
   static constexpr int kES = Op::kES;
   static constexpr int kBK = kRowBytes / kES;             // K elements per k-tile
-  static constexpr int kSteps = kBK / Op::kKStep;          // MFMA k-steps per k-tile (4 or 2)
+  static constexpr int kSteps = kBK / Op::kKStep;          // MFMA k-steps per k-tile (4, 2 or 1)
   static constexpr int kWM = BM / 2, kWN = BN / (NW / 2);  // per-wave output block
   static constexpr int kMI = kWM / kBlk, kNI = kWN / kBlk;  // MFMA blocks per wave
-  // kDMA: k-tiles go global -> LDS directly (buffer_load ... lds), all chunks of k-tile
-  // kt+2 issued in the last MFMA step of k-tile kt; else through the staging registers
+  // kDMA: k-tiles go global -> LDS directly (buffer_load ... lds; with 4 waves all chunks of
+  // k-tile kt+2 issued in the last MFMA step of k-tile kt); else through the staging registers
   // over the first kWriteSteps steps. Measured: direct transfers win for fp8 (they free the
   // staging registers, which fp8's 32-byte fragments need) and for 16-bit operands with
   // 8 waves (the staging registers do not fit next to two waves' accumulators); with 4

@@ -59,3 +59,16 @@ def test_cold_sets_copy_inputs_and_share_outputs():
         assert s[0] is not A and torch.equal(s[0], A) and s[0].data_ptr() != A.data_ptr()
         assert s[2] is not C and torch.equal(s[2], C)
         assert s[3] is D
+
+
+def test_code_text_drops_comments_and_layout_only():
+    # the traffic counters stay valid across comment and layout edits, not across code edits
+    a = "int x = 1;  // one\n/* block\n comment */\nfloat y = x * 2;  \n\n"
+    b = "// new header\nint   x = 1;\n\n  float y = x * 2; /* tail */\n"
+    c = "int x = 2;\nfloat y = x * 2;\n"
+    assert bench.code_text(a) == bench.code_text(b) == "int x = 1;\nfloat y = x * 2;"
+    assert bench.code_text(c) != bench.code_text(a)
+    # comment markers inside string and character literals are code
+    s = 'const char* u = "a//b/*c*/"; char q = \'"\'; int z; // gone'
+    assert bench.code_text(s) == 'const char* u = "a//b/*c*/"; char q = \'"\'; int z;'
+    assert len(bench.source_hash()) == 16
