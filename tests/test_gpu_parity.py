@@ -251,6 +251,27 @@ def test_dact_varlen_and_device_alpha():
     check_close(p, post, tol, rms, "PostAct")
 
 
+@pytest.mark.parametrize("tile", [(128, 128), (256, 256)])
+def test_small_dact_fp8(tile):
+    # fp8 operands through the activation-backward kernels, dense and varlen-M (the 256x256
+    # tiles take the 8-wave 16x16x128 loop, with a partly empty last M-block)
+    M, N, K = 296, 392, 256
+    A, sa = W.quantize_fp8(54, (1, M, K), "e4m3")
+    B, sb = W.quantize_fp8(55, (1, N, K), "e5m2")
+    inp = W.Inputs("dact_fp8", M, N, K, 1, "e4m3", "e5m2", A, B, C=W.normal(1054, (1, M, N), "bf16", 1.5),
+                   c_dt="bf16", d_dt="bf16", post_dt="bf16", act="gelu_tanh", alpha=sa * sb, dact=True)
+    compare_full(inp, tile=tile)
+    sizes = np.array([0, 300, 129, 0, 255])
+    cu = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    M, G = int(cu[-1]), len(sizes)
+    A, sa = W.quantize_fp8(56, (M, K), "e5m2")
+    B, sb = W.quantize_fp8(57, (G, N, K), "e4m3")
+    inp = W.Inputs("dact_fp8_varlen", M, N, K, G, "e5m2", "e4m3", A, B, C=W.normal(1056, (M, N), "bf16", 1.5),
+                   c_dt="bf16", d_dt="bf16", post_dt="bf16", act="silu", alpha=sa * sb, dact=True,
+                   cu_seqlens=cu)
+    compare_full(inp, tile=tile)
+
+
 def test_workload_dact_4096():
     full_size(W.dact_4096())
 
