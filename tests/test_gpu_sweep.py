@@ -130,9 +130,17 @@ def draw_case(i):
     inp.post_dt = out_dt if post else "none"
     inp.act, inp.alpha, inp.beta = act, alpha, beta
     grouped = mode != "dense"
+    # the activation-backward epilogue (C is the pre-activation), where it is built: dense or
+    # varlen-M, no gathered rows, N-major outputs (drawn last, so the other draws of a case
+    # do not depend on it)
+    inp.dact = (mode in ("dense", "varlen_m") and not gather and c_dt != "none"
+                and not (m_major_out and not grouped) and bool(r.random() < 0.35))
+    if inp.dact:
+        inp.beta = beta = 1.0  # beta has no role there, and the boundary asks for 1
+        inp.d_dt = out_dt      # D (the gradient) is that epilogue's required output
     desc = (f"case {i}: {mode} gather={gather} {a_dt}x{b_dt} M={inp.M} N={N} K={inp.K} L={inp.L} "
             f"a_mmaj={a_mmaj} b_nmaj={b_nmaj} tile={tile} C={c_dt} D={inp.d_dt} Post={inp.post_dt} "
-            f"act={act} alpha={alpha} beta={beta} m_major_out={m_major_out}"
+            f"act={act} alpha={alpha} beta={beta} m_major_out={m_major_out} dact={inp.dact}"
             + (f" cu={inp.cu_seqlens.tolist()}" if inp.cu_seqlens is not None else "")
             + (f" cu_k={inp.cu_seqlens_k.tolist()}" if inp.cu_seqlens_k is not None else ""))
     return inp, tile, m_major_out and not grouped, desc
