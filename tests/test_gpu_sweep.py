@@ -3,8 +3,10 @@ batched, varlen-M, varlen-K, with or without gathered A), operand types and majo
 a tile, output types, a C term, an activation, alpha / beta and ragged sizes within the
 alignment rules, runs it through the C ABI and compares every output element with the
 oracle (per element |gpu - oracle| <= tol (|oracle| + 1), plus the normalised-RMS guard).
-The case description is printed before each GPU call.
+The case description is printed before each GPU call. GEP_SWEEP_CASES sets the number of
+cases (default 160; case i draws from seed 9000 + i, so a larger count adds cases).
 """
+import os
 import sys
 
 import numpy as np
@@ -16,7 +18,7 @@ from parity import check_close, oracle_codes, problem_of, run_hip, tol_for
 
 pytestmark = pytest.mark.gpu
 
-CASES = 160
+CASES = int(os.environ.get("GEP_SWEEP_CASES", "160"))
 
 
 def aligned(r, lo, hi, unit):
