@@ -297,6 +297,8 @@ struct TileLoader {
 #if defined(__HIP_DEVICE_COMPILE__)  // the builtin exists for the gfx950 pass only
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (GEP_LDS void*)(lds + (Q * NW + wave) * 1024), 16,
                                              k0 + Q * kDK < klim ? offv[Q] : kOOB, 0, 0, 0);
+#else
+    (void)rs, (void)k0, (void)lds, (void)wave;
 #endif
   }
 
