@@ -16,7 +16,7 @@ constexpr int wg_per_cu() { return BM == 256 ? 1 : 2; }
 // blocks) with global -> LDS transfers; on 32x32 blocks 8 waves had measured +2% on the 8192^3
 // GEMM, +4% on the 4096^3 GEMM with C and GELU, +0.5-2.5% on varlen-M against 4 (the epilogue
 // halves; the store drain moves into the next tile's first wait); fp8 on 16x16x128 blocks
-// +3% on 8192^3 against 4 waves on 32x32x64 (on 32x32x64, 8 waves had been 4% slower). Every
+// +3.7% on 8192^3 against 4 waves on 32x32x64 (on 32x32x64, 8 waves had been 4% slower). Every
 // other kernel runs 4. With 8 waves and transfers the M/N-major kernels ran at half speed
 // (batched 2048x2048x4096x16 550 vs 1125 TFLOP/s, varlen-K 544 vs 1108): their transposed
 // fragment reads (two ds_read_b64_tr_b16 per fragment) grow to 1.5x as many per CU with
